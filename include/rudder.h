@@ -1,0 +1,186 @@
+/*
+ * rudder.h -- C ABI of the stream-aware W4A8 / W4A4 linear layer on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Method: "SteerQuant: Steering Quantization Error with Action-Guided Scaling
+ * in World-Action Models" (paperlayer.ai digest).  A layer keeps ONE static
+ * int4 weight matrix shared by every token stream (video, proprio, action)
+ * and every denoising step (§1, §4.2); a shared positive diagonal rescales the
+ * weights and inversely rescales the activations (§4.2); activations are
+ * quantized with a step size per (stream, denoising step) taken from a
+ * layer-step lookup table (§4.3); the fused kernels apply the scaling inside
+ * activation quantization and follow the low-bit GEMM with dequantization,
+ * inverse-gain compensation and bias, passing only integer activations and
+ * row scales between the two kernels (§4.4, Rudder).  Bit widths: 4-bit
+ * weights, 8- or 4-bit activations (App. D).
+ *
+ * Arithmetic (all fp32 steps round to nearest even):
+ *   inv_smooth[k] = fl32(1 / s[k])                       (formed in fp64)
+ *   w'[k][n]      = W[k][n] * s[k]
+ *   w_scale[n]    = fl32(max_k |w'[k][n]| / 7)           (formed in fp64)
+ *   qw[k][n]      = rne(clamp(w'[k][n] * fl32(1 / w_scale[n]), -7, 7))
+ *   u             = X[m][k] * inv_smooth[k]
+ *   qa[m][k]      = rne(clamp(u * fl32(1 / D[s]), -Qa, Qa)),  s = stream_id[m]
+ *   row_scale[m]  = D[s]
+ *   acc[m][n]     = sum_k qa[m][k] * qw[k][n]            (exact int32)
+ *   y             = fmaf(a[s][n], (float)acc * (row_scale[m] * w_scale[n]), b[s][n])
+ *   Y[m][n]       = bf16_rne(y)
+ * with Qa = 127 (abits = 8) or 7 (abits = 4).  A zero scale has reciprocal 0
+ * (its codes are 0 and its rows give Y = bf16(b)).
+ *
+ * ---------------------------------------------------------------------------
+ * Conventions
+ *   - Every buffer pointer is a DEVICE pointer (hipMalloc'd or torch CUDA
+ *     memory) unless stated otherwise; `stream` is a hipStream_t passed as
+ *     void* (NULL = the default stream).
+ *   - The caller owns and allocates every buffer; the library keeps no device
+ *     state and never allocates.
+ *   - Calls are asynchronous: they return once the work is enqueued on
+ *     `stream`; results are valid after the stream is synchronized.  Calls
+ *     are thread-safe.
+ *   - Arguments are validated on the host before anything is launched; on a
+ *     non-OK return nothing has been enqueued.  rudder_last_error() gives a
+ *     thread-local description of the last failure.
+ *   - Buffers read or written with vector accesses must be 16-byte aligned
+ *     (each call lists them); a misaligned one gives RUDDER_ERR_INVALID_ARG.
+ *   - Undefined behaviour (not checked): stream_id[m] >= S, non-finite X, W,
+ *     s, scales or compensation values, overlapping output buffers.
+ *
+ * Packed-code layout ("MFMA-tiled"), shared by weight codes and activation
+ * codes.  A code matrix C[R][K] (R = N for weights, M for activations) is cut
+ * into 32 x 32 blocks.  Block (rb, kb) -- rows 32rb..32rb+31, k
+ * 32kb..32kb+31 -- is stored contiguously at block index rb * (K/32) + kb.
+ * Inside a block, slot l = (r % 32) + 32 * ((k % 32) / 16), l = 0..63, holds
+ * the 16 codes of row r at k = 32kb + 16*(l/32) + j, j = 0..15:
+ *   - 8-bit codes: 16 bytes, byte j = code j (two's complement);
+ *     block = 1024 bytes;
+ *   - 4-bit codes: 8 bytes = two little-endian 32-bit "split-nibble words",
+ *     word w = j / 8 covering codes 8w..8w+7; byte i (0..3) of a word holds
+ *     code 8w+i in bits 0..3 and code 8w+4+i in bits 4..7, as two's-
+ *     complement nibbles; block = 512 bytes.
+ * Rows from R up to the next multiple of 32 are padding and hold code 0.
+ * ---------------------------------------------------------------------------
+ */
+#ifndef RUDDER_H
+#define RUDDER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    RUDDER_OK = 0,
+    RUDDER_ERR_INVALID_ARG = 1,   /* null required pointer, bad sizes or bit width */
+    RUDDER_ERR_UNSUPPORTED = 2,   /* valid request outside the built shapes */
+    RUDDER_ERR_HIP = 3            /* the HIP runtime reported a launch error */
+} rudder_status_t;
+
+#define RUDDER_MAX_STREAMS 8      /* S, the number of token streams, is 1..8 */
+#define RUDDER_MAX_K 65536        /* keeps every scaled int32 accumulator exact */
+
+/* Bytes of packed weight codes for a K x N layer (K, N multiples of 32):
+ * N * K / 2.  Returns 0 for invalid sizes. */
+size_t rudder_packed_weight_bytes(int K, int N);
+
+/* Bytes of activation codes for M rows (rounded up to 32) of K channels:
+ * ceil(M/32)*32 * K * abits / 8.  Returns 0 for invalid sizes. */
+size_t rudder_packed_act_bytes(int M, int K, int abits);
+
+/* Bytes of device workspace rudder_quant_act needs in dynamic mode. */
+size_t rudder_quant_act_workspace_bytes(int S);
+
+/*
+ * Offline weight preparation (SteerQuant Fig. 2, offline weight preparation;
+ * §4.2 shared-weight error routing).  Folds the smoothing diagonal into the
+ * weights and quantizes each output channel to symmetric int4.
+ *
+ *   W          bf16 bits [K][N], row-major (input channel k, output channel n)
+ *   smooth     fp32 [K], s[k] > 0
+ *   K, N       > 0, multiples of 32
+ *   Wq         out: rudder_packed_weight_bytes(K, N) bytes, 4-bit MFMA-tiled
+ *              layout with R = N (row = output channel)
+ *   w_scale    out: fp32 [N]
+ *   inv_smooth out: fp32 [K] = fl32(1 / s[k]), formed in fp64; this is what
+ *              rudder_quant_act takes for the same layer
+ * Errors: INVALID_ARG for a null pointer, K or N <= 0, K or N not a multiple
+ * of 32, Wq/smooth/w_scale/inv_smooth not 16-byte aligned; UNSUPPORTED for
+ * K > RUDDER_MAX_K.
+ */
+rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
+                                        uint8_t* Wq, float* w_scale, float* inv_smooth,
+                                        void* stream);
+
+/*
+ * Fused activation quantization (SteerQuant §4.4: scaling and stream gains
+ * applied during activation quantization; §4.3: one step size per stream and
+ * denoising step from the layer-step table).
+ *
+ *   X          bf16 bits [M][K], row-major
+ *   stream_id  uint8 [M], each < S (row m belongs to stream stream_id[m])
+ *   inv_smooth fp32 [K] from rudder_quantize_weights
+ *   act_scale  fp32 [S]: the step sizes D[s] of this (layer, step), i.e. the
+ *              table row of the current step.  NULL selects dynamic mode:
+ *              D[s] = fl32(max |u| over the rows of stream s / Qa) (fp64
+ *              divide); a stream with no rows gets D = 0.
+ *   act_scale_out  fp32 [S], dynamic mode: receives D (may be NULL); ignored
+ *              in static mode
+ *   workspace  dynamic mode: rudder_quant_act_workspace_bytes(S) bytes of
+ *              device scratch; ignored (may be NULL) in static mode
+ *   M >= 0 (M = 0 is a no-op), K > 0 multiple of 32, 1 <= S <= 8,
+ *   abits in {4, 8}
+ *   Xq         out: rudder_packed_act_bytes(M, K, abits) bytes, MFMA-tiled
+ *              layout with R = M (8-bit or 4-bit codes); padding rows are 0
+ *   row_scale  out: fp32 [M], row_scale[m] = D[stream_id[m]]
+ * Errors: INVALID_ARG for null X/stream_id/inv_smooth/Xq/row_scale, a null
+ * workspace in dynamic mode, M < 0, K <= 0, K % 32 != 0, S outside 1..8,
+ * abits not 4 or 8, X/inv_smooth/Xq/workspace not 16-byte aligned;
+ * UNSUPPORTED for K > RUDDER_MAX_K.
+ * Dynamic mode enqueues three kernels (partial absmax, finalize, quantize);
+ * static mode one.
+ */
+rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
+                                 const float* inv_smooth, const float* act_scale,
+                                 float* act_scale_out, void* workspace,
+                                 int M, int K, int S, int abits,
+                                 void* Xq, float* row_scale, void* stream);
+
+/*
+ * Low-bit GEMM with fused epilogue (SteerQuant §4.4: low-bit GEMM followed by
+ * dequantization, inverse-gain compensation and bias; §1: Rudder fuses the
+ * output compensation into the low-bit kernel).
+ *
+ *   Xq, row_scale, stream_id   from rudder_quant_act (same M, K, abits)
+ *   Wq, w_scale                from rudder_quantize_weights (same K, N)
+ *   comp_a, comp_b  fp32 [S][N]: the compensation of this (layer, step);
+ *              y = a * t + b as one fp32 fma, the layer bias folded into b
+ *   M >= 0 (M = 0 is a no-op), N > 0 multiple of 32, K > 0 multiple of 128,
+ *   1 <= S <= 8, abits in {4, 8}
+ *   Y          out: bf16 bits [M][N], row-major
+ *   acc_out    optional out: int32 [M][N] row-major raw accumulators
+ *              sum_k qa*qw (a verification aid; pass NULL on the hot path)
+ * Errors: INVALID_ARG for a null required pointer, M < 0, N or K <= 0,
+ * N % 32 != 0, S outside 1..8, abits not 4 or 8, Xq/Wq/w_scale/comp_a/
+ * comp_b/Y/acc_out not 16-byte aligned; UNSUPPORTED for K % 128 != 0 or
+ * K > RUDDER_MAX_K.
+ */
+rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint8_t* stream_id,
+                              const uint8_t* Wq, const float* w_scale,
+                              const float* comp_a, const float* comp_b,
+                              int M, int N, int K, int S, int abits,
+                              uint16_t* Y, int32_t* acc_out, void* stream);
+
+/* Static string naming a status code. */
+const char* rudder_status_string(rudder_status_t status);
+
+/* Thread-local description of the last non-OK return on this thread
+ * ("" if none).  The pointer stays valid until the next call on the thread. */
+const char* rudder_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RUDDER_H */

@@ -1,0 +1,157 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/rudder.h declares, sizes its buffers as documented,
+and rejects invalid arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from tiled_layout import tile_codes, untile_codes
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from w4a4_quantized_gemm_rudder_amd import rudder
+    return rudder.load_library()
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "rudder.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(rudder_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    from w4a4_quantized_gemm_rudder_amd import rudder
+    names = header_functions()
+    assert set(names) == set(rudder.EXPORTED)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_size_helpers(lib):
+    from w4a4_quantized_gemm_rudder_amd import rudder as r
+    assert r.packed_weight_bytes(2048, 6144) == 2048 * 6144 // 2
+    assert r.packed_weight_bytes(100, 64) == 0
+    assert r.packed_act_bytes(4192, 2048, 8) == 4192 * 2048          # 4192 = 131 * 32
+    assert r.packed_act_bytes(96, 256, 4) == 96 * 128
+    assert r.packed_act_bytes(1, 128, 8) == 32 * 128                  # padded to 32 rows
+    assert r.packed_act_bytes(0, 128, 8) == 0
+    assert r.packed_act_bytes(10, 128, 5) == 0
+    assert r.quant_act_workspace_bytes(3) >= 4 * 8 * 2
+
+
+def test_status_strings(lib):
+    lib_ = lib
+    assert lib_.rudder_status_string(0) == b"RUDDER_OK"
+    assert lib_.rudder_status_string(1) == b"RUDDER_ERR_INVALID_ARG"
+    assert lib_.rudder_status_string(2) == b"RUDDER_ERR_UNSUPPORTED"
+    assert lib_.rudder_status_string(3) == b"RUDDER_ERR_HIP"
+
+
+# Fake (never dereferenced) device addresses: every call below fails host
+# validation before any HIP call is made.
+P = 0x1000
+
+
+def _linear(lib, **kw):
+    args = dict(Xq=P, rs=P, sid=P, Wq=P, ws=P, a=P, b=P, M=64, N=256, K=256, S=3, abits=8,
+                Y=P, acc=None)
+    args.update(kw)
+    return lib.rudder_linear(args["Xq"], args["rs"], args["sid"], args["Wq"], args["ws"],
+                             args["a"], args["b"], args["M"], args["N"], args["K"], args["S"],
+                             args["abits"], args["Y"], args["acc"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(Xq=None), 1), (dict(rs=None), 1), (dict(sid=None), 1), (dict(Wq=None), 1),
+    (dict(ws=None), 1), (dict(a=None), 1), (dict(b=None), 1), (dict(Y=None), 1),
+    (dict(M=-1), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(N=48), 1),
+    (dict(S=0), 1), (dict(S=9), 1), (dict(abits=5), 1), (dict(abits=16), 1),
+    (dict(K=96), 2), (dict(K=65536 + 128), 2),
+])
+def test_linear_rejects(lib, kw, status):
+    assert _linear(lib, **kw) == status
+    assert len(lib.rudder_last_error()) > 0
+
+
+def test_linear_m0_is_noop(lib):
+    assert _linear(lib, M=0) == 0
+    assert lib.rudder_last_error() == b""
+
+
+def _quant_act(lib, **kw):
+    args = dict(X=P, sid=P, inv=P, scale=P, out=None, ws=None, M=64, K=256, S=3, abits=8,
+                Xq=P, rs=P)
+    args.update(kw)
+    return lib.rudder_quant_act(args["X"], args["sid"], args["inv"], args["scale"], args["out"],
+                                args["ws"], args["M"], args["K"], args["S"], args["abits"],
+                                args["Xq"], args["rs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(X=None), 1), (dict(sid=None), 1), (dict(inv=None), 1), (dict(Xq=None), 1),
+    (dict(rs=None), 1), (dict(scale=None, ws=None), 1),
+    (dict(M=-5), 1), (dict(K=0), 1), (dict(K=48), 1), (dict(S=0), 1), (dict(S=9), 1),
+    (dict(abits=2), 1), (dict(K=65536 + 32), 2),
+])
+def test_quant_act_rejects(lib, kw, status):
+    assert _quant_act(lib, **kw) == status
+
+
+def test_quant_act_m0_is_noop(lib):
+    assert _quant_act(lib, M=0) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(W=None), 1), (dict(K=0), 1), (dict(N=-32), 1), (dict(K=40), 1), (dict(N=40), 1),
+    (dict(K=65536 + 32), 2),
+])
+def test_quantize_weights_rejects(lib, kw, status):
+    args = dict(W=P, s=P, K=256, N=256, Wq=P, ws=P, inv=P)
+    args.update(kw)
+    assert lib.rudder_quantize_weights(args["W"], args["s"], args["K"], args["N"], args["Wq"],
+                                       args["ws"], args["inv"], None) == status
+
+
+def test_binding_raises_with_message(lib):
+    from w4a4_quantized_gemm_rudder_amd import rudder
+    with pytest.raises(rudder.RudderError) as ei:
+        rudder.rudder_linear(P, P, P, P, P, P, P, 64, 256, 96, 3, 8, P, None, stream=0)
+    assert ei.value.status == rudder.RUDDER_ERR_UNSUPPORTED
+    assert "K=96" in str(ei.value)
+
+
+# The test-side tiling helper must follow the header's definition.
+@pytest.mark.parametrize("bits", [8, 4])
+def test_tiled_layout_roundtrip_and_slots(bits):
+    rng = np.random.default_rng(0)
+    R, K = 45, 96
+    lim = 127 if bits == 8 else 7
+    c = rng.integers(-lim, lim + 1, (R, K)).astype(np.int8)
+    buf = tile_codes(c, bits)
+    assert buf.size == 64 * K * bits // 8          # 45 rows padded to 64
+    back = untile_codes(buf, R, K, bits)
+    assert np.array_equal(back[:R], c) and np.all(back[R:] == 0)
+    # spot-check one slot by hand: row 37, k = 32*2 + 16 + j  ->  block 1*3+2, slot 5+32
+    block = 1 * (K // 32) + 2
+    slot = (37 % 32) + 32
+    slot_bytes = 2 * bits
+    base = (block * 64 + slot) * slot_bytes
+    codes = c[37, 80:96]
+    if bits == 8:
+        assert buf[base:base + 16].view(np.int8).tolist() == codes.tolist()
+    else:
+        b = buf[base:base + 8]
+        assert (b[0] & 0xF) == (codes[0] & 0xF) and (b[0] >> 4) == (codes[4] & 0xF)
+        assert (b[5] & 0xF) == (codes[9] & 0xF) and (b[5] >> 4) == (codes[13] & 0xF)
+
+
+def test_misaligned_rejected(lib):
+    assert _linear(lib, Y=P + 8) == 1
+    assert _linear(lib, Wq=P + 4) == 1
+    assert _quant_act(lib, X=P + 2) == 1

@@ -1,0 +1,278 @@
+// Quantization kernels: offline weight preparation and the fused activation
+// quantizer.
+//
+// SteerQuant ("SteerQuant: Steering Quantization Error with Action-Guided
+// Scaling in World-Action Models", paperlayer.ai digest):
+//   Fig. 2 / §4.2  -- the shared smoothing diagonal is folded into one static
+//                     int4 weight matrix per layer, prepared offline;
+//   §4.3 / §4.4    -- activations are scaled (inverse diagonal, per-(stream,
+//                     step) step size) inside the activation quantizer, which
+//                     emits integer codes plus one scale per row.
+//
+// Both kernels are HBM-streaming codecs: no MFMA work, coalesced 16-byte
+// loads of bf16 and contiguous stores of the MFMA-tiled code layout.
+#include "rudder_internal.h"
+
+namespace rudder {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPartials = 1024;          // dynamic-mode partial-absmax blocks
+
+// ---------------------------------------------------------------------------
+// Weight preparation: one block per 32 output channels.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void quantize_weights_kernel(
+    const uint16_t* __restrict__ W, const float* __restrict__ smooth, int K, int N,
+    uint8_t* __restrict__ Wq, float* __restrict__ w_scale, float* __restrict__ inv_smooth) {
+    __shared__ float s_amax[8][32];
+    __shared__ float s_inv_w[32];
+
+    const int tid = threadIdx.x;
+    const int j = tid & 31;            // channel within the block
+    const int g = tid >> 5;            // k interleave group 0..7
+    const int n = blockIdx.x * 32 + j;
+
+    // inv_smooth: spread over the whole grid.
+    for (int k = blockIdx.x * kThreads + tid; k < K; k += gridDim.x * kThreads)
+        inv_smooth[k] = (float)(1.0 / (double)smooth[k]);
+
+    // Column absmax of w' = W * s.
+    float amax = 0.0f;
+    for (int k = g; k < K; k += 8) {
+        float w = bf16_bits_to_float(W[(size_t)k * N + n]) * smooth[k];
+        amax = fmaxf(amax, fabsf(w));
+    }
+    s_amax[g][j] = amax;
+    __syncthreads();
+    if (g == 0) {
+        float a = s_amax[0][j];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) a = fmaxf(a, s_amax[i][j]);
+        float ws = (float)((double)a / 7.0);
+        w_scale[n] = ws;
+        s_inv_w[j] = step_reciprocal(ws);
+    }
+    __syncthreads();
+
+    // Codes: slot q -> (channel n0 + q % 32, 16 k starting at 16 * (q / 32)).
+    const int slots = 32 * (K / 16);
+    for (int q = tid; q < slots; q += kThreads) {
+        const int jj = q & 31;
+        const int nn = blockIdx.x * 32 + jj;
+        const int k0 = 16 * (q >> 5);
+        const float iw = s_inv_w[jj];
+        int c[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int k = k0 + i;
+            float w = bf16_bits_to_float(W[(size_t)k * N + nn]) * smooth[k];
+            c[i] = quantize_clamped(w * iw, 7.0f);
+        }
+        uint2 out;
+        out.x = split_nibble_word(c);
+        out.y = split_nibble_word(c + 8);
+        *reinterpret_cast<uint2*>(Wq + tiled_slot_offset<4>(nn, k0, K)) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Activation quantizer.  One wave per 32 x 32 (row, k) block of the tiled
+// output: lane l handles row 32rb + l % 32 and the 16 k starting at
+// 32kb + 16 (l / 32), so each wave writes one contiguous code block.
+// ---------------------------------------------------------------------------
+template <int ABITS>
+__global__ __launch_bounds__(kThreads) void quant_act_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ sid,
+    const float* __restrict__ inv_smooth, const float* __restrict__ delta, int M, int K, int S,
+    uint8_t* __restrict__ Xq, float* __restrict__ row_scale) {
+    __shared__ float s_delta[RUDDER_MAX_STREAMS];
+    __shared__ float s_ia[RUDDER_MAX_STREAMS];
+    const int tid = threadIdx.x;
+    if (tid < RUDDER_MAX_STREAMS) {
+        float d = tid < S ? delta[tid] : 0.0f;
+        s_delta[tid] = d;
+        s_ia[tid] = step_reciprocal(d);
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int kblocks = K >> 5;
+    const int total = ((M + 31) >> 5) * kblocks;
+    const int gw = blockIdx.x * (kThreads / 64) + (tid >> 6);
+    if (gw >= total) return;
+    const int rb = gw / kblocks;
+    const int kb = gw - rb * kblocks;
+    const int r = rb * 32 + (lane & 31);
+    const int k0 = kb * 32 + 16 * (lane >> 5);
+    constexpr float Q = ABITS == 8 ? 127.0f : 7.0f;
+
+    int c[16];
+    if (r < M) {
+        const int s = sid[r] & (RUDDER_MAX_STREAMS - 1);
+        const float ia = s_ia[s];
+        const uint4* xp = reinterpret_cast<const uint4*>(X + (size_t)r * K + k0);
+        const uint4 x0 = xp[0], x1 = xp[1];
+        const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const float4* sp = reinterpret_cast<const float4*>(inv_smooth + k0);
+        const float4 s0 = sp[0], s1 = sp[1], s2 = sp[2], s3 = sp[3];
+        const float is[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                              s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const uint32_t h = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
+            const float u = bf16_bits_to_float(h) * is[i];
+            c[i] = quantize_clamped(u * ia, Q);
+        }
+        if (kb == 0 && lane < 32) row_scale[r] = s_delta[s];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] = 0;
+    }
+
+    if constexpr (ABITS == 8) {
+        uint4 out;
+        out.x = byte_word(c);
+        out.y = byte_word(c + 4);
+        out.z = byte_word(c + 8);
+        out.w = byte_word(c + 12);
+        *reinterpret_cast<uint4*>(Xq + tiled_slot_offset<8>(r, k0, K)) = out;
+    } else {
+        uint2 out;
+        out.x = split_nibble_word(c);
+        out.y = split_nibble_word(c + 8);
+        *reinterpret_cast<uint2*>(Xq + tiled_slot_offset<4>(r, k0, K)) = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Dynamic step sizes: per-stream absmax of u = X * inv_smooth.
+// Pass 1: each block reduces its grid-stride share into partial[block][s]
+// (wave-level butterfly reductions, then across the block's waves in LDS).
+// Pass 2: one block folds the partials and forms D[s] = fl32(amax_s / Qa).
+// max is order-independent, so the result is deterministic.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__global__ __launch_bounds__(kThreads) void act_absmax_partial_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ sid,
+    const float* __restrict__ inv_smooth, int M, int K, float* __restrict__ partial) {
+    __shared__ float s_red[kThreads / 64][RUDDER_MAX_STREAMS];
+    float amax[RUDDER_MAX_STREAMS];
+#pragma unroll
+    for (int s = 0; s < RUDDER_MAX_STREAMS; ++s) amax[s] = 0.0f;
+
+    const int chunks_per_row = K >> 4;
+    const long total = (long)M * chunks_per_row;
+    for (long i = (long)blockIdx.x * kThreads + threadIdx.x; i < total;
+         i += (long)gridDim.x * kThreads) {
+        const int m = (int)(i / chunks_per_row);
+        const int k0 = (int)(i - (long)m * chunks_per_row) * 16;
+        const uint4* xp = reinterpret_cast<const uint4*>(X + (size_t)m * K + k0);
+        const uint4 x0 = xp[0], x1 = xp[1];
+        const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        float cmax = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t h = (e & 1) ? (xw[e >> 1] >> 16) : (xw[e >> 1] & 0xFFFFu);
+            cmax = fmaxf(cmax, fabsf(bf16_bits_to_float(h) * inv_smooth[k0 + e]));
+        }
+        const int s = sid[m] & (RUDDER_MAX_STREAMS - 1);
+#pragma unroll
+        for (int t = 0; t < RUDDER_MAX_STREAMS; ++t)
+            if (t == s) amax[t] = fmaxf(amax[t], cmax);
+    }
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < RUDDER_MAX_STREAMS; ++s) {
+        const float v = wave_max(amax[s]);
+        if (lane == 0) s_red[wave][s] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < RUDDER_MAX_STREAMS) {
+        float v = s_red[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) v = fmaxf(v, s_red[w][threadIdx.x]);
+        partial[blockIdx.x * RUDDER_MAX_STREAMS + threadIdx.x] = v;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void act_scale_finalize_kernel(
+    const float* __restrict__ partial, int nparts, int S, float qa, float* __restrict__ delta,
+    float* __restrict__ act_scale_out) {
+    __shared__ float s_red[kThreads / 64][RUDDER_MAX_STREAMS];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+#pragma unroll
+    for (int s = 0; s < RUDDER_MAX_STREAMS; ++s) {
+        float v = 0.0f;
+        for (int p = threadIdx.x; p < nparts; p += kThreads)
+            v = fmaxf(v, partial[p * RUDDER_MAX_STREAMS + s]);
+        v = wave_max(v);
+        if (lane == 0) s_red[wave][s] = v;
+    }
+    __syncthreads();
+    if (threadIdx.x < RUDDER_MAX_STREAMS) {
+        float v = s_red[0][threadIdx.x];
+#pragma unroll
+        for (int w = 1; w < kThreads / 64; ++w) v = fmaxf(v, s_red[w][threadIdx.x]);
+        const float d = (float)((double)v / (double)qa);
+        delta[threadIdx.x] = d;
+        if (act_scale_out != nullptr && threadIdx.x < S) act_scale_out[threadIdx.x] = d;
+    }
+}
+
+}  // namespace
+
+size_t quant_act_workspace_bytes() {
+    return sizeof(float) * RUDDER_MAX_STREAMS * (kMaxPartials + 1);
+}
+
+hipError_t launch_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
+                                   uint8_t* Wq, float* w_scale, float* inv_smooth,
+                                   hipStream_t stream) {
+    hipLaunchKernelGGL(quantize_weights_kernel, dim3(N / 32), dim3(kThreads), 0, stream, W,
+                       smooth, K, N, Wq, w_scale, inv_smooth);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_static(const uint16_t* X, const uint8_t* sid, const float* inv_smooth,
+                                   const float* delta, int M, int K, int S, int abits, void* Xq,
+                                   float* row_scale, hipStream_t stream) {
+    const long waves = (long)((M + 31) / 32) * (K / 32);
+    const dim3 grid((unsigned)((waves + 3) / 4));
+    if (abits == 8)
+        hipLaunchKernelGGL(quant_act_kernel<8>, grid, dim3(kThreads), 0, stream, X, sid,
+                           inv_smooth, delta, M, K, S, static_cast<uint8_t*>(Xq), row_scale);
+    else
+        hipLaunchKernelGGL(quant_act_kernel<4>, grid, dim3(kThreads), 0, stream, X, sid,
+                           inv_smooth, delta, M, K, S, static_cast<uint8_t*>(Xq), row_scale);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_act_dynamic(const uint16_t* X, const uint8_t* sid,
+                                    const float* inv_smooth, float* act_scale_out,
+                                    void* workspace, int M, int K, int S, int abits, void* Xq,
+                                    float* row_scale, hipStream_t stream) {
+    float* partial = static_cast<float*>(workspace);
+    float* delta = partial + (size_t)kMaxPartials * RUDDER_MAX_STREAMS;
+    const long chunks = (long)M * (K / 16);
+    long nb = (chunks + kThreads - 1) / kThreads;
+    if (nb > kMaxPartials) nb = kMaxPartials;
+    if (nb < 1) nb = 1;
+    hipLaunchKernelGGL(act_absmax_partial_kernel, dim3((unsigned)nb), dim3(kThreads), 0, stream,
+                       X, sid, inv_smooth, M, K, partial);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(act_scale_finalize_kernel, dim3(1), dim3(kThreads), 0, stream, partial,
+                       (int)nb, S, abits == 8 ? 127.0f : 7.0f, delta, act_scale_out);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_quant_act_static(X, sid, inv_smooth, delta, M, K, S, abits, Xq, row_scale,
+                                   stream);
+}
+
+}  // namespace rudder

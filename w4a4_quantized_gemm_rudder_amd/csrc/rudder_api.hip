@@ -1,0 +1,154 @@
+// C ABI of librudder: argument validation, error reporting and dispatch to
+// the kernel launchers.  Nothing is launched unless every check passes.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "rudder_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+rudder_status_t fail(rudder_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+rudder_status_t fail(rudder_status_t st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u); }
+
+rudder_status_t ok() {
+    g_last_error.clear();
+    return RUDDER_OK;
+}
+
+rudder_status_t from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(RUDDER_ERR_HIP, "%s: HIP launch failed: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t rudder_packed_weight_bytes(int K, int N) {
+    if (K <= 0 || N <= 0 || K % 32 || N % 32) return 0;
+    return (size_t)N * (size_t)K / 2;
+}
+
+size_t rudder_packed_act_bytes(int M, int K, int abits) {
+    if (M < 0 || K <= 0 || K % 32 || (abits != 4 && abits != 8)) return 0;
+    const size_t rows = (size_t)((M + 31) / 32) * 32;
+    return rows * (size_t)K * (size_t)abits / 8;
+}
+
+size_t rudder_quant_act_workspace_bytes(int S) {
+    (void)S;
+    return rudder::quant_act_workspace_bytes();
+}
+
+rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
+                                        uint8_t* Wq, float* w_scale, float* inv_smooth,
+                                        void* stream) {
+    const char* f = "rudder_quantize_weights";
+    if (!W || !smooth || !Wq || !w_scale || !inv_smooth)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (K <= 0 || N <= 0)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d and N=%d must be positive", f, K, N);
+    if (K % 32 || N % 32)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d and N=%d must be multiples of 32", f, K, N);
+    if (misaligned(Wq) || misaligned(smooth) || misaligned(w_scale) || misaligned(inv_smooth))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: Wq, smooth, w_scale and inv_smooth must be "
+                    "16-byte aligned", f);
+    if (K > RUDDER_MAX_K)
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
+    return from_hip(rudder::launch_quantize_weights(W, smooth, K, N, Wq, w_scale, inv_smooth,
+                                                    static_cast<hipStream_t>(stream)),
+                    f);
+}
+
+rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
+                                 const float* inv_smooth, const float* act_scale,
+                                 float* act_scale_out, void* workspace, int M, int K, int S,
+                                 int abits, void* Xq, float* row_scale, void* stream) {
+    const char* f = "rudder_quant_act";
+    if (!X || !stream_id || !inv_smooth || !Xq || !row_scale)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (act_scale == nullptr && workspace == nullptr)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: dynamic mode (act_scale NULL) needs a workspace",
+                    f);
+    if (M < 0 || K <= 0)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: M=%d must be >= 0 and K=%d > 0", f, M, K);
+    if (K % 32) return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 32", f, K);
+    if (S < 1 || S > RUDDER_MAX_STREAMS)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: S=%d must be in 1..%d", f, S, RUDDER_MAX_STREAMS);
+    if (abits != 4 && abits != 8)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
+    if (misaligned(X) || misaligned(inv_smooth) || misaligned(Xq) || misaligned(workspace))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: X, inv_smooth, Xq and workspace must be "
+                    "16-byte aligned", f);
+    if (K > RUDDER_MAX_K)
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
+    if (M == 0) return ok();
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (act_scale != nullptr)
+        return from_hip(rudder::launch_quant_act_static(X, stream_id, inv_smooth, act_scale, M, K,
+                                                        S, abits, Xq, row_scale, st),
+                        f);
+    return from_hip(rudder::launch_quant_act_dynamic(X, stream_id, inv_smooth, act_scale_out,
+                                                     workspace, M, K, S, abits, Xq, row_scale, st),
+                    f);
+}
+
+rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint8_t* stream_id,
+                              const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                              const float* comp_b, int M, int N, int K, int S, int abits,
+                              uint16_t* Y, int32_t* acc_out, void* stream) {
+    const char* f = "rudder_linear";
+    if (!Xq || !row_scale || !stream_id || !Wq || !w_scale || !comp_a || !comp_b || !Y)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (M < 0 || N <= 0 || K <= 0)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: M=%d must be >= 0, N=%d and K=%d > 0", f, M, N,
+                    K);
+    if (N % 32) return fail(RUDDER_ERR_INVALID_ARG, "%s: N=%d must be a multiple of 32", f, N);
+    if (S < 1 || S > RUDDER_MAX_STREAMS)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: S=%d must be in 1..%d", f, S, RUDDER_MAX_STREAMS);
+    if (abits != 4 && abits != 8)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
+    if (misaligned(Xq) || misaligned(Wq) || misaligned(w_scale) || misaligned(comp_a) ||
+        misaligned(comp_b) || misaligned(Y) || misaligned(acc_out))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: Xq, Wq, w_scale, comp_a, comp_b, Y and acc_out "
+                    "must be 16-byte aligned", f);
+    if (K % 128)
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d is not a multiple of 128", f, K);
+    if (K > RUDDER_MAX_K)
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
+    if (M == 0) return ok();
+    return from_hip(rudder::launch_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b,
+                                          M, N, K, S, abits, Y, acc_out,
+                                          static_cast<hipStream_t>(stream)),
+                    f);
+}
+
+const char* rudder_status_string(rudder_status_t status) {
+    switch (status) {
+        case RUDDER_OK: return "RUDDER_OK";
+        case RUDDER_ERR_INVALID_ARG: return "RUDDER_ERR_INVALID_ARG";
+        case RUDDER_ERR_UNSUPPORTED: return "RUDDER_ERR_UNSUPPORTED";
+        case RUDDER_ERR_HIP: return "RUDDER_ERR_HIP";
+    }
+    return "RUDDER_ERR_UNKNOWN";
+}
+
+const char* rudder_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

@@ -1,0 +1,91 @@
+// Internal declarations shared by the HIP translation units of librudder.
+// Device helpers here implement the arithmetic stated in include/rudder.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "rudder.h"
+
+namespace rudder {
+
+// ---------------------------------------------------------------------------
+// Launch-side entry points (one per kernel family).  Arguments are already
+// validated by the C ABI layer; each returns the launch's hipError_t.
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
+                                   uint8_t* Wq, float* w_scale, float* inv_smooth,
+                                   hipStream_t stream);
+
+hipError_t launch_quant_act_static(const uint16_t* X, const uint8_t* sid, const float* inv_smooth,
+                                   const float* delta, int M, int K, int S, int abits, void* Xq,
+                                   float* row_scale, hipStream_t stream);
+
+hipError_t launch_quant_act_dynamic(const uint16_t* X, const uint8_t* sid,
+                                    const float* inv_smooth, float* act_scale_out,
+                                    void* workspace, int M, int K, int S, int abits, void* Xq,
+                                    float* row_scale, hipStream_t stream);
+
+size_t quant_act_workspace_bytes();
+
+hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* sid,
+                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                         const float* comp_b, int M, int N, int K, int S, int abits, uint16_t* Y,
+                         int32_t* acc_out, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Device helpers
+// ---------------------------------------------------------------------------
+
+// bf16 bits -> fp32 (exact: bf16 is the upper half of an fp32 pattern).
+__device__ __forceinline__ float bf16_bits_to_float(uint32_t h) {
+    return __uint_as_float(h << 16);
+}
+
+// fp32 -> bf16 bits with round-to-nearest-even (finite inputs).
+__device__ __forceinline__ uint32_t float_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Reciprocal of a step size: formed in fp64, rounded once to fp32; 0 -> 0.
+__device__ __forceinline__ float step_reciprocal(float d) {
+    return d > 0.0f ? (float)(1.0 / (double)d) : 0.0f;
+}
+
+// Symmetric quantizer: clamp to [-q, q], round half to even.
+__device__ __forceinline__ int quantize_clamped(float v, float q) {
+    v = fminf(fmaxf(v, -q), q);
+    return (int)__builtin_rintf(v);
+}
+
+// Pack 8 codes (k0..k7) into one split-nibble word: byte i holds code i in
+// bits 0..3 and code i+4 in bits 4..7.
+__device__ __forceinline__ uint32_t split_nibble_word(const int* c) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        uint32_t b = ((uint32_t)c[i] & 0xFu) | (((uint32_t)c[i + 4] & 0xFu) << 4);
+        w |= b << (8 * i);
+    }
+    return w;
+}
+
+// Pack 4 int8 codes into a 32-bit word, byte i = code i.
+__device__ __forceinline__ uint32_t byte_word(const int* c) {
+    return ((uint32_t)c[0] & 0xFFu) | (((uint32_t)c[1] & 0xFFu) << 8) |
+           (((uint32_t)c[2] & 0xFFu) << 16) | (((uint32_t)c[3] & 0xFFu) << 24);
+}
+
+// Byte offset of slot (row r, k) in an MFMA-tiled code matrix with K columns.
+// Slot = 16 codes; bytes per slot = 16 (8-bit) or 8 (4-bit).
+template <int BITS>
+__device__ __forceinline__ size_t tiled_slot_offset(int r, int k, int K) {
+    constexpr int SLOT_BYTES = 2 * BITS;           // 16 codes * BITS / 8
+    constexpr int BLOCK_BYTES = 64 * SLOT_BYTES;
+    size_t block = (size_t)(r >> 5) * (size_t)(K >> 5) + (size_t)(k >> 5);
+    int slot = (r & 31) + 32 * ((k & 31) >> 4);
+    return block * BLOCK_BYTES + (size_t)slot * SLOT_BYTES;
+}
+
+}  // namespace rudder

@@ -1,0 +1,322 @@
+"""Benchmark of the stream-aware W4A8/W4A4 linear on one MI355X.
+
+A step is one denoising step's quantized linear set of a DiT block at
+hidden 2048 over 2 rollouts x 4192 tokens (8384 rows: 8192 video, 64
+proprio, 128 action): QKV 2048->6144 and O 2048->2048 at W4A8, MLP up
+2048->8192 and down 8192->2048 at W4A4.  Each linear is one
+rudder_quant_act (fused smoothing + per-(stream, step) quantization) and one
+rudder_linear (int8-MFMA GEMM + fused dequant/compensation epilogue), i.e. 8
+launches per step; the step index cycles through the 16-step denoise loop,
+selecting that step's activation step sizes and compensation vectors
+(SteerQuant §4.3 layer-step table, §4.4 Rudder).  Weights are prepared once
+before timing (offline preparation, SteerQuant Fig. 2).  All inputs are
+seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line.  `value` is whole-step throughput in TOPS (2*M*N*K
+summed over the four linears, per second, both kernels of each linear
+included); `us_per_step` is the latency of one step.  `roofline` describes
+the kernel that takes the most time per step, timed live with HIP events
+around each of its launches on the launch stream.  `cpu_baseline` times the
+CPU oracle on a bounded sample of the same step.
+
+--workload picks another workload (each printed as one JSON line of the
+same form, steps cycling through its step-indexed scale sets).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("fused W4A8/W4A4 linear TOPS and % int8-MFMA peak; "
+          "µs per denoising-step layer set")
+INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published
+HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
+DEFAULT_WORKLOAD = "dit_block_h2048_m8384_16step"
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["w4a4_quantized_gemm_rudder_amd/csrc/w4_gemm.hip",
+                  "w4a4_quantized_gemm_rudder_amd/csrc/quantize.hip",
+                  "w4a4_quantized_gemm_rudder_amd/csrc/rudder_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=32)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-bf16", action="store_true", help="skip the bf16 matmul comparator")
+    p.add_argument("--cpu-rows", type=int, default=8384,
+                   help="rows per linear in the CPU-oracle sample")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="before warmup, run a plain device copy of this many bytes three "
+                        "times (a known-size reference for HBM byte counters)")
+    return p.parse_args()
+
+
+def _to_dev_bf16(bits, torch):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def _to_dev(a, torch):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def prepare(wl_name: str, seed: int, torch, rudder, W):
+    wi = W.make_inputs(wl_name, seed=seed)
+    wl = wi.workload
+    S = wl.S
+    M = wl.M
+    sid_d = _to_dev(wi.stream_id, torch)
+    xs = {}
+    layers = []
+    for L in wi.layers:
+        key = id(L.x)
+        if key not in xs:
+            xs[key] = _to_dev_bf16(L.x, torch)
+        X = xs[key]
+        Wd = _to_dev_bf16(L.w, torch)
+        s_d = _to_dev(L.smooth, torch)
+        Wq, ws, inv = rudder.quantize_weights(Wd, s_d)
+        abits = L.layer.abits
+        K, N = L.layer.K, L.layer.N
+        if L.act_scale is not None:
+            delta = _to_dev(L.act_scale, torch)                       # [T, S]
+        else:
+            delta = None
+        comp_a = _to_dev(L.comp_a, torch)
+        comp_b = _to_dev(L.comp_b, torch)
+        Xq = torch.empty(rudder.packed_act_bytes(M, K, abits), dtype=torch.uint8, device="cuda")
+        rs = torch.empty(M, dtype=torch.float32, device="cuda")
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        wsp = torch.empty(rudder.quant_act_workspace_bytes(S), dtype=torch.uint8, device="cuda")
+        layers.append(dict(name=L.layer.name, K=K, N=N, abits=abits, X=X, Wbf16=Wd, Wq=Wq,
+                           w_scale=ws, inv=inv, delta=delta, comp_a=comp_a, comp_b=comp_b,
+                           Xq=Xq, rs=rs, Y=Y, ws=wsp, src=L))
+    return wi, sid_d, layers
+
+
+def run_step(t: int, wl, sid_d, layers, rudder, ev=None):
+    """Enqueue one step (all linears).  ev: optional list of (start, end)
+    event pairs per layer, recorded around the GEMM launch."""
+    S, M = wl.S, wl.M
+    T = wl.n_steps
+    tt = t % T
+    for i, Ly in enumerate(layers):
+        K, N, abits = Ly["K"], Ly["N"], Ly["abits"]
+        if Ly["delta"] is None:
+            rudder.rudder_quant_act(Ly["X"], sid_d, Ly["inv"], None, None, Ly["ws"], M, K, S,
+                                    abits, Ly["Xq"], Ly["rs"])
+        else:
+            rudder.rudder_quant_act(Ly["X"], sid_d, Ly["inv"], Ly["delta"][tt], None, None, M, K,
+                                    S, abits, Ly["Xq"], Ly["rs"])
+        ca = Ly["comp_a"][tt] if Ly["comp_a"].dim() == 3 else Ly["comp_a"]
+        cb = Ly["comp_b"][tt] if Ly["comp_b"].dim() == 3 else Ly["comp_b"]
+        if ev is not None:
+            ev[i][0].record()
+        rudder.rudder_linear(Ly["Xq"], Ly["rs"], sid_d, Ly["Wq"], Ly["w_scale"], ca, cb, M, N, K,
+                             S, abits, Ly["Y"], None)
+        if ev is not None:
+            ev[i][1].record()
+
+
+def load_traffic(kernel_tag: str, src_hash: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    path = os.path.join(PROFILE_DIR, "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(kernel_tag)
+    if not ent or ent.get("source_hash") != src_hash:
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(wi, rows_per_layer: int, seed: int):
+    """Time the CPU oracle (quantize -> integer GEMM -> epilogue) on a
+    bounded row sample of one step of the workload."""
+    import oracle
+    wl = wi.workload
+    rng = np.random.default_rng(seed)
+    M = wl.M
+    rows = np.sort(rng.choice(M, size=min(rows_per_layer, M), replace=False))
+    sid = np.ascontiguousarray(wi.stream_id[rows])
+    prepared = []
+    for L in wi.layers:
+        inv = oracle.inv_smooth(L.smooth)
+        qw, ws = oracle.quantize_weights(L.w, L.smooth)          # offline, untimed
+        x = np.ascontiguousarray(L.x[rows])
+        prepared.append((L, inv, qw, ws, x))
+    ops = 0
+    t0 = time.perf_counter()
+    for (L, inv, qw, ws, x) in prepared:
+        if L.act_scale is None:
+            delta = oracle.dynamic_scales(x, sid, inv, wl.S, L.layer.abits)
+        else:
+            delta = L.act_scale[0]
+        a, b = L.step_comp(0)
+        oracle.linear(x, sid, qw, ws, inv, delta, a, b, wl.S, L.layer.abits)
+        ops += 2 * len(rows) * L.layer.K * L.layer.N
+    dt = time.perf_counter() - t0
+    return dict(value=ops / dt / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
+                sample=f"{len(rows)} of {M} rows through all {len(wi.layers)} linears of "
+                       f"step 0 (quantize + int32 GEMM + epilogue), {dt:.1f} s wall")
+
+
+def bf16_comparator(wl, layers, torch, reps: int = 10):
+    """torch.matmul in bf16 (hipBLASLt) on the same [M,K] x [K,N] shapes."""
+    M = wl.M
+    tot = 0.0
+    for Ly in layers:
+        A = Ly["X"]
+        B = Ly["Wbf16"]
+        for _ in range(3):
+            torch.matmul(A, B)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.matmul(A, B)
+        e1.record()
+        torch.cuda.synchronize()
+        tot += e0.elapsed_time(e1) / reps
+    del M
+    return tot * 1e3      # µs per step
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the layer shards by "
+              "rows or output channels with no exchange, but no multi-GPU path is built.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from w4a4_quantized_gemm_rudder_amd import rudder
+    from w4a4_quantized_gemm_rudder_amd import workloads as W
+    rudder.load_library()
+    torch.cuda.set_device(0)
+
+    wi, sid_d, layers = prepare(args.workload, args.seed, torch, rudder, W)
+    wl = wi.workload
+    torch.cuda.synchronize()
+
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for t in range(args.warmup):
+        run_step(t, wl, sid_d, layers, rudder)
+    torch.cuda.synchronize()
+
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers] for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_wall0 = time.perf_counter()
+    start.record()
+    for t in range(args.steps):
+        run_step(t, wl, sid_d, layers, rudder, ev[t])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    # per-kernel (GEMM) launch durations, grouped by kernel instance (abits)
+    gemm_ms = {}
+    gemm_ops = {}
+    for t in range(args.steps):
+        for i, Ly in enumerate(layers):
+            d = ev[t][i][0].elapsed_time(ev[t][i][1])
+            key = f"w4a{Ly['abits']}_gemm"
+            gemm_ms.setdefault(key, []).append(d)
+            gemm_ops.setdefault(key, []).append(2 * wl.M * Ly["N"] * Ly["K"])
+    dominant = max(gemm_ms, key=lambda k: sum(gemm_ms[k]))
+    avg_ms = float(np.mean(gemm_ms[dominant]))
+    ops_per_launch = float(np.mean(gemm_ops[dominant]))
+    achieved = ops_per_launch / (avg_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
+    traffic = load_traffic(f"{dominant}_{args.workload}", src_hash)
+
+    ops_step = wl.ops_per_step()
+    value = ops_step / (ms_per_step * 1e-3) / 1e12
+    gemm_only_ms = sum(sum(v) for v in gemm_ms.values()) / args.steps
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_step": round(ms_per_step * 1e3, 1),
+        "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
+        "gemm_only_tops": round(ops_step / (gemm_only_ms * 1e-3) / 1e12, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "tokens": wl.M,
+            "streams": {W.STREAM_NAMES[s]: int((wi.stream_id == s).sum()) for s in range(wl.S)},
+            "linears": [f"{Ly['name']} {Ly['K']}->{Ly['N']} W4A{Ly['abits']}" for Ly in layers],
+            "denoise_steps": wl.n_steps,
+            "launches_per_step": 2 * len(layers) + (2 * len(layers) if wl.dynamic else 0),
+        },
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": INT8_PEAK_TOPS,
+            "unit": "TFLOP/s",
+            "op_count": "2*M*N*K int8 multiply-add ops (TOPS)",
+            "frac": round(achieved / INT8_PEAK_TOPS, 4),
+            "traffic": traffic,
+            "avg_launch_us": round(avg_ms * 1e3, 2),
+            "ops_per_launch": ops_per_launch,
+            "source_hash": src_hash,
+        },
+        "wall_s": round(wall, 3),
+    }
+    if not args.no_bf16:
+        bf16_us = bf16_comparator(wl, layers, torch)
+        out["bf16_matmul_us_per_step"] = round(bf16_us, 1)
+        out["speedup_vs_bf16_matmul"] = round(bf16_us / (ms_per_step * 1e3), 3)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.seed)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

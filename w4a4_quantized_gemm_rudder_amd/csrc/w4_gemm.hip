@@ -8,17 +8,29 @@
 //
 // gfx950 mapping
 //   * v_mfma_i32_32x32x32_i8: the MFMA "A" operand is a 32-channel slice of
-//     the weights (output channel n = MFMA row i), the "B" operand a 32-row
+//     the weights (output channel n = MFMA row i), the "B" operand a 32-token
 //     slice of the activations (token m = MFMA column j), so each lane's
 //     accumulators hold one token row and runs of 4 consecutive channels.
 //   * There is no int4 MFMA.  4-bit codes are widened in registers: the
-//     split-nibble word w turns into (w << 4) & 0xF0F0F0F0 and w & 0xF0F0F0F0,
-//     i.e. bytes equal to 16 * code, in natural k order.  The int32 result is
-//     then 16x (W4A8) or 256x (W4A4) the true accumulator, which is exact for
-//     K <= RUDDER_MAX_K and is undone with an arithmetic shift.
-//   * Codes arrive in the MFMA-tiled layout, so every global -> LDS copy is a
-//     contiguous 16-byte-per-lane stream and every LDS read of a fragment is
-//     a contiguous lane-ordered 8- or 16-byte access (no bank conflicts).
+//     split-nibble word w becomes (w << 4) & 0xF0F0F0F0 and w & 0xF0F0F0F0,
+//     bytes equal to 16 * code in natural k order.  The int32 result is then
+//     16x (W4A8) or 256x (W4A4) the true accumulator -- exact for
+//     K <= RUDDER_MAX_K -- and an arithmetic shift undoes it.
+//   * Codes arrive MFMA-tiled (32 x 32 blocks in lane order), so global ->
+//     LDS traffic uses the gfx950 direct-to-LDS 16-byte loads (no VGPR
+//     staging, one contiguous KiB per wave instruction) into an NS-stage LDS
+//     ring, and every fragment read is a contiguous lane-ordered ds_read.
+//   * One workgroup barrier per k-stage: loads for stage kt+NS-1 are issued
+//     right after the barrier that retires stage kt-1's buffer.
+//   * Epilogue: dequantize + compensate in registers, stage the bf16 tile in
+//     LDS (XOR-swizzled 16-byte chunks), then store whole 512-byte row
+//     segments with 16-byte stores so every HBM line is written once.
+//   * Tile order: workgroups are dealt round-robin to the 8 XCDs; the grid is
+//     remapped so each XCD walks a contiguous, m-grouped range of tiles and
+//     the tiles in flight on one XCD share activation and weight panels in
+//     that XCD's L2.
+#include <type_traits>
+
 #include "rudder_internal.h"
 
 namespace rudder {
@@ -26,23 +38,44 @@ namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BM = 256;          // tokens per block tile
 constexpr int BN = 256;          // output channels per block tile
 constexpr int BK = 128;          // k per pipeline stage (4 MFMA k-steps)
-constexpr int kWaves = 8;        // 2 (n) x 4 (m) waves, wave tile 128 n x 64 m
+constexpr int kWavesN = 4;       // waves along the channel dimension
+constexpr int kWavesM = 2;       // waves along the token dimension
+constexpr int kWaves = kWavesN * kWavesM;
 constexpr int kThreads = 64 * kWaves;
+constexpr int FW = BN / kWavesN / 32;   // 32-channel fragments per wave (2)
+constexpr int FA = BM / kWavesM / 32;   // 32-token fragments per wave (4)
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;       // m-tiles per tile group (L2 reuse of weight panels)
 
-// LDS bytes of one stage
-template <int ABITS>
-struct Stage {
-    static constexpr int kActBlock = 64 * 2 * ABITS;               // 1024 or 512
-    static constexpr int kActBytes = (BM / 32) * (BK / 32) * kActBlock;
+template <int ABITS, int NS>
+struct Cfg {
+    static constexpr int kActBlock = 64 * 2 * ABITS;                 // 1024 / 512 bytes
+    static constexpr int kActPerMb = (BK / 32) * kActBlock;          // per 32-token block
+    static constexpr int kActBytes = (BM / 32) * kActPerMb;          // 32 / 16 KiB
     static constexpr int kWBlock = 512;
-    static constexpr int kWBytes = (BN / 32) * (BK / 32) * kWBlock;
-    static constexpr int kActLoads = kActBytes / (16 * kThreads);  // 16-byte loads per thread
-    static constexpr int kWLoads = kWBytes / (16 * kThreads);
+    static constexpr int kWPerNb = (BK / 32) * kWBlock;              // 2 KiB
+    static constexpr int kWBytes = (BN / 32) * kWPerNb;              // 16 KiB
+    static constexpr int kStageBytes = kActBytes + kWBytes;
+    static constexpr int kRingBytes = NS * kStageBytes;
+    // 16-byte direct loads per thread per stage (each wave instruction = 1 KiB)
+    static constexpr int kActLoads = kActBytes / (1024 * kWaves);
+    static constexpr int kWLoads = kWBytes / (1024 * kWaves);
+    static constexpr int kLoads = kActLoads + kWLoads;
+    static constexpr int kEpiBytes = BM * BN * 2;                    // bf16 tile, 128 KiB
+    // Per-tile epilogue tables (w_scale, comp_a[S], comp_b[S] for the tile's
+    // 256 channels, 1 KiB each) live after both the ring and the bf16 tile.
+    static constexpr int kTableOffset = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
+    static constexpr int lds_bytes(int S) { return kTableOffset + (1 + 2 * S) * 1024; }
 };
+
+// Number of ring stages for a bit width and stream count: the deepest ring
+// whose LDS (ring + tables) fits the 160 KiB of a gfx950 CU.
+constexpr int kLdsLimit = 160 * 1024;
 
 __device__ __forceinline__ v4i widen_nibbles(uint32_t w0, uint32_t w1) {
     v4i r;
@@ -53,148 +86,316 @@ __device__ __forceinline__ v4i widen_nibbles(uint32_t w0, uint32_t w1) {
     return r;
 }
 
+// Two fp32 -> packed bf16 with round-to-nearest-even (gfx950 hardware
+// conversion; finite inputs): low half = a, high half = b.
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+    uint32_t r;
+    asm("v_cvt_pk_bf16_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Direct-to-LDS 16-byte load: lane l reads 16 bytes at sbase + voff(l)
+// (wave-uniform 64-bit base in SGPRs, 32-bit per-lane offset) and the wave
+// writes them lane-linearly at LDS offset `lds` (M0).  Written as inline asm
+// so the compiler does not add its own conservative vmcnt waits in front of
+// LDS reads; the kernel orders these loads itself with wait_and_barrier().
+// The instruction has no VGPR results.
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, uint32_t lds) {
+    // the base is wave-uniform by construction; make that explicit so it
+    // is always held in SGPRs
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    const void* sbase = reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "memory");
+}
+
+// Wait until this wave's LDS reads are complete and at most N of its
+// vector-memory loads are in flight, then barrier the workgroup: afterwards
+// every wave's loads up to that point have landed in LDS, and no wave still
+// reads the buffer that the next loads overwrite.
+template <int N>
+__device__ __forceinline__ void wait_and_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
+}
+
+template <int L>
+__device__ __forceinline__ void wait_stages_and_barrier(int stages_in_flight) {
+    // stages_in_flight is 0..3
+    if (stages_in_flight >= 3) wait_and_barrier<3 * L>();
+    else if (stages_in_flight == 2) wait_and_barrier<2 * L>();
+    else if (stages_in_flight == 1) wait_and_barrier<L>();
+    else wait_and_barrier<0>();
+}
+
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
+// Map the linear workgroup id to (tile_m, tile_n): XCD-contiguous ranges,
+// then groups of kGroupM m-tiles walked column by column.
+__device__ __forceinline__ void tile_of_block(int bid, int nblk, int tiles_m, int tiles_n,
+                                              int& tm, int& tn) {
+    const int xcd = bid % kXcds;
+    const int idx = bid / kXcds;
+    const int per = nblk / kXcds;
+    const int extra = nblk % kXcds;
+    const int t = xcd * per + (xcd < extra ? xcd : extra) + idx;
+    const int group = t / (kGroupM * tiles_n);
+    const int first_m = group * kGroupM;
+    const int gm = min(kGroupM, tiles_m - first_m);
+    const int local = t - group * (kGroupM * tiles_n);
+    tm = first_m + local % gm;
+    tn = local / gm;
+}
+
+// Raw (still packed) fragment words of one 32-wide k-substep.
 template <int ABITS>
+struct RawFrags {
+    uint2 w[FW];                                    // channel blocks x 16 nibbles
+    typename std::conditional<ABITS == 8, uint4, uint2>::type a[FA];  // token blocks
+};
+
+template <int ABITS, int NS>
+__device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, int wn, int wm,
+                                           int lane, RawFrags<ABITS>& fr) {
+    using C = Cfg<ABITS, NS>;
+    const uint8_t* wst = stage + C::kActBytes;
+#pragma unroll
+    for (int f = 0; f < FW; ++f)
+        fr.w[f] = *reinterpret_cast<const uint2*>(wst + (wn * FW + f) * C::kWPerNb +
+                                                  kk * C::kWBlock + lane * 8);
+#pragma unroll
+    for (int g = 0; g < FA; ++g) {
+        const uint8_t* ap = stage + (wm * FA + g) * C::kActPerMb + kk * C::kActBlock;
+        if constexpr (ABITS == 8)
+            fr.a[g] = *reinterpret_cast<const uint4*>(ap + lane * 16);
+        else
+            fr.a[g] = *reinterpret_cast<const uint2*>(ap + lane * 8);
+    }
+}
+
+// Scheduling groups (LLVM AMDGPU sched_group_barrier masks).
+constexpr int kSchedVALU = 0x002;
+constexpr int kSchedMFMA = 0x008;
+constexpr int kSchedDSRead = 0x100;
+
+// One 32-wide k-substep: widen this substep's 4-bit fragments and issue its
+// FW x FA MFMAs.  The LDS reads of the next substep (already issued by the
+// caller, in program order before this call) and the widening ops are
+// interleaved with the MFMAs, so the wave keeps issuing independent work
+// while the matrix pipe is busy instead of stalling on a cluster of MFMAs.
+template <int ABITS>
+__device__ __forceinline__ void mma_substep(const RawFrags<ABITS>& fr, v16i (&acc)[FW][FA]) {
+    v4i wf[FW], af[FA];
+#pragma unroll
+    for (int f = 0; f < FW; ++f) wf[f] = widen_nibbles(fr.w[f].x, fr.w[f].y);
+#pragma unroll
+    for (int g = 0; g < FA; ++g) {
+        if constexpr (ABITS == 8)
+            af[g] = v4i{(int)fr.a[g].x, (int)fr.a[g].y, (int)fr.a[g].z, (int)fr.a[g].w};
+        else
+            af[g] = widen_nibbles(fr.a[g].x, fr.a[g].y);
+    }
+#pragma unroll
+    for (int f = 0; f < FW; ++f)
+#pragma unroll
+        for (int g = 0; g < FA; ++g)
+            acc[f][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[f], af[g], acc[f][g], 0, 0, 0);
+    // Interleave: each MFMA is followed by a few VALU ops and one LDS read.
+    constexpr int kValu = ABITS == 8 ? 6 * FW : 6 * (FW + FA);
+    constexpr int kMfma = FW * FA;
+    constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
+#pragma unroll
+    for (int i = 0; i < kMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSchedVALU, kValuPer, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
+    }
+}
+
+template <int ABITS, int NS, bool ACC_OUT>
 __global__ __launch_bounds__(kThreads, 1) void w4_gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
     const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
-    const float* __restrict__ comp_b, int M, int N, int K, uint16_t* __restrict__ Y,
-    int32_t* __restrict__ acc_out, int tiles_n) {
-    using St = Stage<ABITS>;
-    __shared__ __attribute__((aligned(16))) uint8_t lds_act[St::kActBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_w[St::kWBytes];
+    const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
+    int32_t* __restrict__ acc_out, int tiles_m, int tiles_n) {
+    using C = Cfg<ABITS, NS>;
+    constexpr int L = C::kLoads;
+    extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int wn = wave & 1;          // 128-channel half of the tile
-    const int wm = wave >> 1;         // 64-token quarter of the tile
+    const int wn = wave % kWavesN;    // channel slice of the tile (FW * 32 channels)
+    const int wm = wave / kWavesN;    // token slice of the tile (FA * 32 tokens)
+    const int uwave = __builtin_amdgcn_readfirstlane(wave);   // wave index as a scalar
 
-    const int tile_n = blockIdx.x % tiles_n;
-    const int tile_m = blockIdx.x / tiles_n;
+    int tile_m, tile_n;
+    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tile_m, tile_n);
     const int kblocks = K >> 5;
     const int mblocks = (M + 31) >> 5;
     const int nblocks = N >> 5;
+    const int ksteps = K / BK;
+    const int n_tile0 = min(tile_n * BN, N - 32);            // first channel of the tile (clamped)
 
-    // ---- global source pointers for this thread's 16-byte chunks --------
-    // Activation stage: [mb 0..7][kb 0..3][block]; the 4 k-blocks of one
-    // token block are contiguous in both global memory and LDS.
-    constexpr int kActPerMb = (BK / 32) * St::kActBlock;     // bytes per token block per stage
-    const uint8_t* act_src[St::kActLoads];
-    bool act_ok[St::kActLoads];
+    // Row data of this lane's two token rows, fetched before the main loop
+    // (plain loads; the compiler waits for them only in the epilogue).
+    int row_stream[FA];
+    float row_rs[FA];
 #pragma unroll
-    for (int i = 0; i < St::kActLoads; ++i) {
-        const int c = (i * kThreads + tid) * 16;             // byte offset in stage
-        const int mb = c / kActPerMb;
-        const int rem = c - mb * kActPerMb;
-        const int gmb = tile_m * (BM / 32) + mb;
-        act_ok[i] = gmb < mblocks;
-        act_src[i] = Xq + ((size_t)gmb * kblocks) * St::kActBlock + rem;
-    }
-    constexpr int kWPerNb = (BK / 32) * St::kWBlock;
-    const uint8_t* w_src[St::kWLoads];
-    bool w_ok[St::kWLoads];
-#pragma unroll
-    for (int i = 0; i < St::kWLoads; ++i) {
-        const int c = (i * kThreads + tid) * 16;
-        const int nb = c / kWPerNb;
-        const int rem = c - nb * kWPerNb;
-        const int gnb = tile_n * (BN / 32) + nb;
-        w_ok[i] = gnb < nblocks;
-        w_src[i] = Wq + ((size_t)gnb * kblocks) * St::kWBlock + rem;
+    for (int g = 0; g < FA; ++g) {
+        const int mc = min(tile_m * BM + wm * (FA * 32) + g * 32 + (lane & 31), M - 1);
+        row_stream[g] = sid[mc] & (RUDDER_MAX_STREAMS - 1);
+        row_rs[g] = row_scale[mc];
     }
 
-    uint4 act_reg[St::kActLoads];
-    uint4 w_reg[St::kWLoads];
-    auto load_stage = [&](int kt) {
-        const size_t act_off = (size_t)kt * kActPerMb;
-        const size_t w_off = (size_t)kt * kWPerNb;
+    // ---- epilogue tables -> LDS (one KiB per table row, one wave each) ----
+    // row 0: w_scale, rows 1..S: comp_a[s], rows S+1..2S: comp_b[s], each for
+    // channels n_tile0 .. n_tile0 + 255 (a tile narrower than 256 channels
+    // reads past its last channel only within the same row of the table
+    // when N >= 256; narrower matrices clamp the window to the last 256).
+    const uint32_t lds_base = lds_offset(lds);
+    {
+        const int nwin = N >= BN ? min(n_tile0, N - BN) : 0;
+        const int cols = N >= BN ? BN : N;                   // columns present in the window
+        const int per_lane = cols * 4 / 64;                  // bytes per lane (16 when cols = 256)
+        for (int r = uwave; r < 1 + 2 * S; r += kWaves) {
+            const float* src = r == 0 ? w_scale
+                             : (r <= S ? comp_a + (size_t)(r - 1) * N
+                                       : comp_b + (size_t)(r - 1 - S) * N);
+            const uint32_t dst = lds_base + C::kTableOffset + r * 1024;
+            if (per_lane == 16) {
+                load_lds16(src + nwin, lane * 16, __builtin_amdgcn_readfirstlane(dst));
+            } else {
+                // N < 256: plain loads (rare, small layers)
+                for (int c = lane; c < cols; c += 64)
+                    reinterpret_cast<float*>(lds + C::kTableOffset + r * 1024)[c] = src[c];
+            }
+        }
+    }
+
+    // ---- per-wave direct-load sources ------------------------------------
+    // Each wave instruction moves one contiguous KiB: for activations the
+    // (32-token block, k-block) pairs of this stage, for weights the
+    // (32-channel block, k-block) pairs.  Bases are wave-uniform (SGPRs);
+    // every lane adds lane * 16.  Token / channel blocks past the matrix edge
+    // are clamped to the last real block (their results are never stored).
+    const uint32_t voff = lane * 16;
+    const uint8_t* act_src[C::kActLoads];
+    int act_dst[C::kActLoads];
 #pragma unroll
-        for (int i = 0; i < St::kActLoads; ++i)
-            act_reg[i] = act_ok[i] ? *reinterpret_cast<const uint4*>(act_src[i] + act_off)
-                                   : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < C::kActLoads; ++i) {
+        const int byte = (uwave * C::kActLoads + i) * 1024;   // offset within the stage
+        const int mb = byte / C::kActPerMb;
+        const int rem = byte - mb * C::kActPerMb;
+        const int gmb = min(tile_m * (BM / 32) + mb, mblocks - 1);
+        act_src[i] = Xq + (size_t)gmb * kblocks * C::kActBlock + rem;
+        act_dst[i] = byte;
+    }
+    const uint8_t* w_src[C::kWLoads];
+    int w_dst[C::kWLoads];
 #pragma unroll
-        for (int i = 0; i < St::kWLoads; ++i)
-            w_reg[i] = w_ok[i] ? *reinterpret_cast<const uint4*>(w_src[i] + w_off)
-                               : make_uint4(0, 0, 0, 0);
-    };
-    auto store_stage = [&]() {
+    for (int i = 0; i < C::kWLoads; ++i) {
+        const int byte = (uwave * C::kWLoads + i) * 1024;
+        const int nb = byte / C::kWPerNb;
+        const int rem = byte - nb * C::kWPerNb;
+        const int gnb = min(tile_n * (BN / 32) + nb, nblocks - 1);
+        w_src[i] = Wq + (size_t)gnb * kblocks * C::kWBlock + rem;
+        w_dst[i] = C::kActBytes + byte;
+    }
+
+    auto issue_stage = [&](int kt) {
+        const uint32_t base = lds_base + (uint32_t)((kt % NS) * C::kStageBytes);
+        const size_t a_off = (size_t)kt * C::kActPerMb;
+        const size_t w_off = (size_t)kt * C::kWPerNb;
 #pragma unroll
-        for (int i = 0; i < St::kActLoads; ++i)
-            *reinterpret_cast<uint4*>(lds_act + (i * kThreads + tid) * 16) = act_reg[i];
+        for (int i = 0; i < C::kActLoads; ++i)
+            load_lds16(act_src[i] + a_off, voff, base + act_dst[i]);
 #pragma unroll
-        for (int i = 0; i < St::kWLoads; ++i)
-            *reinterpret_cast<uint4*>(lds_w + (i * kThreads + tid) * 16) = w_reg[i];
+        for (int i = 0; i < C::kWLoads; ++i)
+            load_lds16(w_src[i] + w_off, voff, base + w_dst[i]);
     };
 
-    v16i acc[4][2];
+    v16i acc[FW][FA];
 #pragma unroll
-    for (int f = 0; f < 4; ++f)
+    for (int f = 0; f < FW; ++f)
 #pragma unroll
-        for (int g = 0; g < 2; ++g)
+        for (int g = 0; g < FA; ++g)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0;
 
-    const int ksteps = K / BK;
-    load_stage(0);
+    // ---- main loop ----------------------------------------------------------
+    // Prologue: fill all NS buffers, wait for stage 0.
+    const int pre = min(NS, ksteps);
+    for (int s = 0; s < pre; ++s) issue_stage(s);
+    wait_stages_and_barrier<L>(pre - 1);
+
+    // Fragments are read one k-substep ahead of the MFMAs that use them.  The
+    // barrier that admits stage kt+1 sits after the reads of stage kt's last
+    // substep and before its MFMAs, so the MFMA pipe has work queued while
+    // the workgroup synchronizes and the next stage's first fragments load.
+    // Fragments are read two k-substeps ahead of the MFMAs that use them
+    // (substep kk of every stage uses register set fr[kk]).  The barrier
+    // that admits stage kt+1 sits in stage kt after its last fragment reads,
+    // so the MFMA pipe still has two substeps of work queued while the
+    // workgroup synchronizes and the next stage's first fragments load.
+    RawFrags<ABITS> fr[BK / 32];
+    read_frags<ABITS, NS>(lds, 0, wn, wm, lane, fr[0]);
+    read_frags<ABITS, NS>(lds, 1, wn, wm, lane, fr[1]);
     for (int kt = 0; kt < ksteps; ++kt) {
-        __syncthreads();                       // previous stage fully consumed
-        store_stage();
-        __syncthreads();
-        if (kt + 1 < ksteps) load_stage(kt + 1);
+        const uint8_t* st = lds + (kt % NS) * C::kStageBytes;
+        const uint8_t* st1 = lds + ((kt + 1) % NS) * C::kStageBytes;
 #pragma unroll
         for (int kk = 0; kk < BK / 32; ++kk) {
-            v4i wf[4];
-#pragma unroll
-            for (int f = 0; f < 4; ++f) {
-                const int nb = wn * 4 + f;
-                const uint2 p = *reinterpret_cast<const uint2*>(
-                    lds_w + nb * kWPerNb + kk * St::kWBlock + lane * 8);
-                wf[f] = widen_nibbles(p.x, p.y);
-            }
-            v4i af[2];
-#pragma unroll
-            for (int g = 0; g < 2; ++g) {
-                const int mb = wm * 2 + g;
-                if constexpr (ABITS == 8) {
-                    const uint4 p = *reinterpret_cast<const uint4*>(
-                        lds_act + mb * kActPerMb + kk * St::kActBlock + lane * 16);
-                    af[g] = v4i{(int)p.x, (int)p.y, (int)p.z, (int)p.w};
-                } else {
-                    const uint2 p = *reinterpret_cast<const uint2*>(
-                        lds_act + mb * kActPerMb + kk * St::kActBlock + lane * 8);
-                    af[g] = widen_nibbles(p.x, p.y);
+            if (kk < 2) {
+                read_frags<ABITS, NS>(st, kk + 2, wn, wm, lane, fr[kk + 2]);
+            } else if (kt + 1 < ksteps) {
+                if (kk == 2) {
+                    // stages issued beyond kt+1 that may still be in flight
+                    wait_stages_and_barrier<L>(min(NS - 2, ksteps - 2 - kt));
+                    if (kt + NS < ksteps) issue_stage(kt + NS);
                 }
+                read_frags<ABITS, NS>(st1, kk - 2, wn, wm, lane, fr[kk - 2]);
             }
-#pragma unroll
-            for (int f = 0; f < 4; ++f)
-#pragma unroll
-                for (int g = 0; g < 2; ++g)
-                    acc[f][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[f], af[g], acc[f][g],
-                                                                      0, 0, 0);
+            mma_substep<ABITS>(fr[kk], acc);
         }
     }
 
     // ---- fused epilogue -------------------------------------------------
+    // 1. registers: t = float(acc) * (row_scale * w_scale); y = fma(a, t, b);
+    //    bf16 (hardware round-to-nearest-even pack) into this wave's LDS
+    //    staging area [FA*32 token rows][FW*32 channels]; 16-byte chunk c of
+    //    row r sits at chunk c ^ ((r >> 1) & 7).  Per-channel values come
+    //    from the LDS tables.
+    // 2. each wave stores its own rows: 8 lanes per 128-byte row, so every
+    //    store instruction writes whole cache lines.
     constexpr int kShift = ABITS == 8 ? 4 : 8;
+    constexpr int kWaveRowBytes = FW * 32 * 2;                 // 128
+    constexpr int kWaveRows = FA * 32;                         // 128
+    __syncthreads();                                   // ring no longer read
+    const float* tab = reinterpret_cast<const float*>(lds + C::kTableOffset);
+    const int tab_shift = tile_n * BN - (N >= BN ? min(n_tile0, N - BN) : 0);
+    uint8_t* wstage = lds + wave * (kWaveRows * kWaveRowBytes);
 #pragma unroll
-    for (int g = 0; g < 2; ++g) {
-        const int m = tile_m * BM + wm * 64 + g * 32 + (lane & 31);
-        if (m >= M) continue;
-        const int s = sid[m] & (RUDDER_MAX_STREAMS - 1);
-        const float rs = row_scale[m];
-        const float* ca = comp_a + (size_t)s * N;
-        const float* cb = comp_b + (size_t)s * N;
+    for (int f = 0; f < FW; ++f) {
 #pragma unroll
-        for (int f = 0; f < 4; ++f) {
-            const int n0 = tile_n * BN + wn * 128 + f * 32;
-            if (n0 >= N) continue;
+        for (int q = 0; q < 4; ++q) {
+            const int nl = wn * (FW * 32) + f * 32 + 8 * q + 4 * (lane >> 5);  // channel in tile
+            const int ti = min(nl + tab_shift, 252);           // column in the table window
+            const float4 ws = *reinterpret_cast<const float4*>(tab + ti);
+            const int chunk = f * 4 + q;                       // 16-byte chunk in the wave row
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int n = n0 + 8 * q + 4 * (lane >> 5);
-                const float4 ws = *reinterpret_cast<const float4*>(w_scale + n);
-                const float4 a = *reinterpret_cast<const float4*>(ca + n);
-                const float4 b = *reinterpret_cast<const float4*>(cb + n);
+            for (int g = 0; g < FA; ++g) {
+                const int s = row_stream[g];
+                const float rs = row_rs[g];
+                const float4 a = *reinterpret_cast<const float4*>(tab + 256 * (1 + s) + ti);
+                const float4 b = *reinterpret_cast<const float4*>(tab + 256 * (1 + S + s) + ti);
                 const int v0 = acc[f][g][4 * q + 0] >> kShift;
                 const int v1 = acc[f][g][4 * q + 1] >> kShift;
                 const int v2 = acc[f][g][4 * q + 2] >> kShift;
@@ -204,15 +405,71 @@ __global__ __launch_bounds__(kThreads, 1) void w4_gemm_kernel(
                 const float y2 = __builtin_fmaf(a.z, (float)v2 * (rs * ws.z), b.z);
                 const float y3 = __builtin_fmaf(a.w, (float)v3 * (rs * ws.w), b.w);
                 uint2 packed;
-                packed.x = float_to_bf16_bits(y0) | (float_to_bf16_bits(y1) << 16);
-                packed.y = float_to_bf16_bits(y2) | (float_to_bf16_bits(y3) << 16);
-                *reinterpret_cast<uint2*>(Y + (size_t)m * N + n) = packed;
-                if (acc_out != nullptr)
-                    *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n) =
-                        make_int4(v0, v1, v2, v3);
+                packed.x = pack_bf16x2_rne(y0, y1);
+                packed.y = pack_bf16x2_rne(y2, y3);
+                const int r = g * 32 + (lane & 31);
+                *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes +
+                                          ((chunk ^ ((r >> 1) & 7)) * 16) + (lane >> 5) * 8) =
+                    packed;
+                if constexpr (ACC_OUT) {
+                    const int m = tile_m * BM + wm * kWaveRows + r;
+                    const int n = tile_n * BN + nl;
+                    if (m < M && n < N)
+                        *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n) =
+                            make_int4(v0, v1, v2, v3);
+                }
             }
         }
+        // keep the accumulator reads of one fragment column together
+        // (bounds the registers the epilogue needs)
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // 2. whole-line stores of this wave's rows (its own LDS writes are
+    //    ordered before these reads)
+    const int c = lane & 7;
+    const int m0 = tile_m * BM + wm * kWaveRows;
+    const int n = tile_n * BN + wn * (FW * 32) + c * 8;
+#pragma unroll 4
+    for (int i = 0; i < kWaveRows / 8; ++i) {
+        const int r = i * 8 + (lane >> 3);
+        const uint4 v = *reinterpret_cast<const uint4*>(wstage + r * kWaveRowBytes +
+                                                        ((c ^ ((r >> 1) & 7)) * 16));
+        if (m0 + r < M && n < N)
+            *reinterpret_cast<uint4*>(Y + (size_t)(m0 + r) * N + n) = v;
+    }
+}
+
+template <int ABITS, int NS, bool ACC_OUT>
+hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                          const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
+                          int32_t* acc_out, hipStream_t stream) {
+    using C = Cfg<ABITS, NS>;
+    static_assert(C::lds_bytes(1) <= kLdsLimit, "LDS budget");
+    static const hipError_t attr = hipFuncSetAttribute(
+        (const void*)w4_gemm_kernel<ABITS, NS, ACC_OUT>,
+        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+    if (attr != hipSuccess) return attr;
+    const int tiles_m = (M + BM - 1) / BM;
+    const int tiles_n = (N + BN - 1) / BN;
+    hipLaunchKernelGGL((w4_gemm_kernel<ABITS, NS, ACC_OUT>), dim3((unsigned)(tiles_m * tiles_n)),
+                       dim3(kThreads), C::lds_bytes(S), stream, xq, row_scale, sid, Wq, w_scale,
+                       comp_a, comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n);
+    return hipGetLastError();
+}
+
+template <int ABITS, bool ACC_OUT>
+hipError_t launch_bits(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+                       const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                       const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
+                       int32_t* acc_out, hipStream_t stream) {
+    // deepest ring that fits together with this call's tables
+    constexpr int NS_MAX = ABITS == 8 ? 3 : 4;
+    if (Cfg<ABITS, NS_MAX>::lds_bytes(S) <= kLdsLimit)
+        return launch_variant<ABITS, NS_MAX, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                      comp_b, M, N, K, S, Y, acc_out, stream);
+    return launch_variant<ABITS, NS_MAX - 1, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                      comp_b, M, N, K, S, Y, acc_out, stream);
 }
 
 }  // namespace
@@ -221,18 +478,19 @@ hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* 
                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
                          const float* comp_b, int M, int N, int K, int S, int abits, uint16_t* Y,
                          int32_t* acc_out, hipStream_t stream) {
-    (void)S;
-    const int tiles_m = (M + BM - 1) / BM;
-    const int tiles_n = (N + BN - 1) / BN;
-    const dim3 grid((unsigned)(tiles_m * tiles_n));
     const uint8_t* xq = static_cast<const uint8_t*>(Xq);
-    if (abits == 8)
-        hipLaunchKernelGGL(w4_gemm_kernel<8>, grid, dim3(kThreads), 0, stream, xq, row_scale,
-                           sid, Wq, w_scale, comp_a, comp_b, M, N, K, Y, acc_out, tiles_n);
-    else
-        hipLaunchKernelGGL(w4_gemm_kernel<4>, grid, dim3(kThreads), 0, stream, xq, row_scale,
-                           sid, Wq, w_scale, comp_a, comp_b, M, N, K, Y, acc_out, tiles_n);
-    return hipGetLastError();
+    if (abits == 8) {
+        if (acc_out)
+            return launch_bits<8, true>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
+                                        S, Y, acc_out, stream);
+        return launch_bits<8, false>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S,
+                                     Y, acc_out, stream);
+    }
+    if (acc_out)
+        return launch_bits<4, true>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S,
+                                    Y, acc_out, stream);
+    return launch_bits<4, false>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S, Y,
+                                 acc_out, stream);
 }
 
 }  // namespace rudder

@@ -40,11 +40,12 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int BM = 256;          // tokens per block tile
+constexpr int BM = 128;          // tokens per block tile
 constexpr int BN = 256;          // output channels per block tile
 constexpr int BK = 128;          // k per pipeline stage (4 MFMA k-steps)
 constexpr int kWavesN = 4;       // waves along the channel dimension
-constexpr int kWavesM = 2;       // waves along the token dimension
+constexpr int kWavesM = 1;       // waves along the token dimension
+constexpr int kBlocksPerCU = 2;  // two independent workgroups share each CU
 constexpr int kWaves = kWavesN * kWavesM;
 constexpr int kThreads = 64 * kWaves;
 constexpr int FW = BN / kWavesN / 32;   // 32-channel fragments per wave (2)
@@ -66,16 +67,15 @@ struct Cfg {
     static constexpr int kActLoads = kActBytes / (1024 * kWaves);
     static constexpr int kWLoads = kWBytes / (1024 * kWaves);
     static constexpr int kLoads = kActLoads + kWLoads;
-    static constexpr int kEpiBytes = BM * BN * 2;                    // bf16 tile, 128 KiB
+    static constexpr int kEpiBytes = BM * BN * 2;                    // bf16 tile
     // Per-tile epilogue tables (w_scale, comp_a[S], comp_b[S] for the tile's
     // 256 channels, 1 KiB each) live after both the ring and the bf16 tile.
     static constexpr int kTableOffset = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
     static constexpr int lds_bytes(int S) { return kTableOffset + (1 + 2 * S) * 1024; }
 };
 
-// Number of ring stages for a bit width and stream count: the deepest ring
-// whose LDS (ring + tables) fits the 160 KiB of a gfx950 CU.
-constexpr int kLdsLimit = 160 * 1024;
+// LDS per workgroup: the 160 KiB of a gfx950 CU shared by kBlocksPerCU.
+constexpr int kLdsLimit = 160 * 1024 / kBlocksPerCU;
 
 __device__ __forceinline__ v4i widen_nibbles(uint32_t w0, uint32_t w1) {
     v4i r;
@@ -107,9 +107,10 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, uint
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
     const void* sbase = reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+    const uint32_t slds = __builtin_amdgcn_readfirstlane(lds);
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
                  :
-                 : "v"(voff), "s"(sbase), "s"(lds)
+                 : "v"(voff), "s"(sbase), "s"(slds)
                  : "memory");
 }
 
@@ -125,8 +126,9 @@ __device__ __forceinline__ void wait_and_barrier() {
 
 template <int L>
 __device__ __forceinline__ void wait_stages_and_barrier(int stages_in_flight) {
-    // stages_in_flight is 0..3
-    if (stages_in_flight >= 3) wait_and_barrier<3 * L>();
+    // stages_in_flight is 0..4
+    if (stages_in_flight >= 4) wait_and_barrier<4 * L>();
+    else if (stages_in_flight == 3) wait_and_barrier<3 * L>();
     else if (stages_in_flight == 2) wait_and_barrier<2 * L>();
     else if (stages_in_flight == 1) wait_and_barrier<L>();
     else wait_and_barrier<0>();
@@ -219,7 +221,7 @@ __device__ __forceinline__ void mma_substep(const RawFrags<ABITS>& fr, v16i (&ac
 }
 
 template <int ABITS, int NS, bool ACC_OUT>
-__global__ __launch_bounds__(kThreads, 1) void w4_gemm_kernel(
+__global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
     const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
@@ -341,29 +343,41 @@ __global__ __launch_bounds__(kThreads, 1) void w4_gemm_kernel(
     // substep and before its MFMAs, so the MFMA pipe has work queued while
     // the workgroup synchronizes and the next stage's first fragments load.
     // Fragments are read two k-substeps ahead of the MFMAs that use them
-    // (substep kk of every stage uses register set fr[kk]).  The barrier
-    // that admits stage kt+1 sits in stage kt after its last fragment reads,
-    // so the MFMA pipe still has two substeps of work queued while the
-    // workgroup synchronizes and the next stage's first fragments load.
-    RawFrags<ABITS> fr[BK / 32];
-    read_frags<ABITS, NS>(lds, 0, wn, wm, lane, fr[0]);
-    read_frags<ABITS, NS>(lds, 1, wn, wm, lane, fr[1]);
-    for (int kt = 0; kt < ksteps; ++kt) {
-        const uint8_t* st = lds + (kt % NS) * C::kStageBytes;
-        const uint8_t* st1 = lds + ((kt + 1) % NS) * C::kStageBytes;
+    // (global substep j = kt * P + kk uses register set fr[j % 4]).  The
+    // barrier that admits stage kt+1 sits right before the first read of
+    // that stage, after every read of stage kt, so the MFMA pipe still has
+    // queued substeps while the workgroup synchronizes.
+    constexpr int P = BK / 32;                       // substeps per stage
+    constexpr int D = 2;                             // read-ahead distance
+    constexpr int U = 4 / P;                         // stages per unrolled iteration
+    static_assert(P * U == 4 && D <= P * U, "substep bookkeeping");
+    RawFrags<ABITS> fr[4];
 #pragma unroll
-        for (int kk = 0; kk < BK / 32; ++kk) {
-            if (kk < 2) {
-                read_frags<ABITS, NS>(st, kk + 2, wn, wm, lane, fr[kk + 2]);
-            } else if (kt + 1 < ksteps) {
-                if (kk == 2) {
-                    // stages issued beyond kt+1 that may still be in flight
-                    wait_stages_and_barrier<L>(min(NS - 2, ksteps - 2 - kt));
-                    if (kt + NS < ksteps) issue_stage(kt + NS);
+    for (int j = 0; j < D; ++j)
+        read_frags<ABITS, NS>(lds + (j / P) * C::kStageBytes, j % P, wn, wm, lane, fr[j]);
+    for (int kt0 = 0; kt0 < ksteps; kt0 += U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int kt = kt0 + u;
+            if (kt < ksteps) {
+#pragma unroll
+                for (int kk = 0; kk < P; ++kk) {
+                    const int j = u * P + kk;                // substep index mod 4
+                    const int ahead = kk + D;                // substep to read, relative to stage kt
+                    const int rk = ahead % P;
+                    const int rst = kt + ahead / P;          // its stage
+                    if (rst < ksteps) {
+                        if (ahead / P == 1 && rk == 0) {
+                            // first read of stage kt+1: admit it, refill the ring
+                            wait_stages_and_barrier<L>(min(NS - 2, ksteps - 2 - kt));
+                            if (kt + NS < ksteps) issue_stage(kt + NS);
+                        }
+                        read_frags<ABITS, NS>(lds + (rst % NS) * C::kStageBytes, rk, wn, wm,
+                                              lane, fr[(j + D) % 4]);
+                    }
+                    mma_substep<ABITS>(fr[j], acc);
                 }
-                read_frags<ABITS, NS>(st1, kk - 2, wn, wm, lane, fr[kk - 2]);
             }
-            mma_substep<ABITS>(fr[kk], acc);
         }
     }
 
@@ -446,9 +460,12 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
                           int32_t* acc_out, hipStream_t stream) {
     using C = Cfg<ABITS, NS>;
     static_assert(C::lds_bytes(1) <= kLdsLimit, "LDS budget");
+    static_assert(C::lds_bytes(RUDDER_MAX_STREAMS) <= 160 * 1024, "LDS budget");
+    // the attribute admits the full CU; a call whose tables do not fit the
+    // per-workgroup share simply runs fewer workgroups per CU
     static const hipError_t attr = hipFuncSetAttribute(
         (const void*)w4_gemm_kernel<ABITS, NS, ACC_OUT>,
-        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsLimit);
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
@@ -464,11 +481,12 @@ hipError_t launch_bits(const uint8_t* xq, const float* row_scale, const uint8_t*
                        const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                        int32_t* acc_out, hipStream_t stream) {
     // deepest ring that fits together with this call's tables
-    constexpr int NS_MAX = ABITS == 8 ? 3 : 4;
+    constexpr int NS_MAX = ABITS == 8 ? 2 : 3;
     if (Cfg<ABITS, NS_MAX>::lds_bytes(S) <= kLdsLimit)
         return launch_variant<ABITS, NS_MAX, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
                                                       comp_b, M, N, K, S, Y, acc_out, stream);
-    return launch_variant<ABITS, NS_MAX - 1, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
+    constexpr int NS_MIN = NS_MAX > 2 ? NS_MAX - 1 : 2;
+    return launch_variant<ABITS, NS_MIN, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
                                                       comp_b, M, N, K, S, Y, acc_out, stream);
 }
 

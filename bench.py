@@ -66,6 +66,8 @@ def parse_args():
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 matmul comparator")
     p.add_argument("--cpu-rows", type=int, default=8384,
                    help="rows per linear in the CPU-oracle sample")
+    p.add_argument("--cpu-steps", type=int, default=6,
+                   help="denoising steps in the CPU-oracle sample")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="before warmup, run a plain device copy of this many bytes three "
                         "times (a known-size reference for HBM byte counters)")
@@ -152,9 +154,10 @@ def load_traffic(kernel_tag: str, src_hash: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(wi, rows_per_layer: int, seed: int):
+def cpu_baseline(wi, rows_per_layer: int, n_steps: int, seed: int):
     """Time the CPU oracle (quantize -> integer GEMM -> epilogue) on a
-    bounded row sample of one step of the workload."""
+    bounded sample of the workload: rows_per_layer rows through every linear
+    for the first n_steps step-indexed scale sets."""
     import oracle
     wl = wi.workload
     rng = np.random.default_rng(seed)
@@ -167,20 +170,23 @@ def cpu_baseline(wi, rows_per_layer: int, seed: int):
         qw, ws = oracle.quantize_weights(L.w, L.smooth)          # offline, untimed
         x = np.ascontiguousarray(L.x[rows])
         prepared.append((L, inv, qw, ws, x))
+    steps = max(1, min(n_steps, wl.n_steps))
     ops = 0
     t0 = time.perf_counter()
-    for (L, inv, qw, ws, x) in prepared:
-        if L.act_scale is None:
-            delta = oracle.dynamic_scales(x, sid, inv, wl.S, L.layer.abits)
-        else:
-            delta = L.act_scale[0]
-        a, b = L.step_comp(0)
-        oracle.linear(x, sid, qw, ws, inv, delta, a, b, wl.S, L.layer.abits)
-        ops += 2 * len(rows) * L.layer.K * L.layer.N
+    for t in range(steps):
+        for (L, inv, qw, ws, x) in prepared:
+            if L.act_scale is None:
+                delta = oracle.dynamic_scales(x, sid, inv, wl.S, L.layer.abits)
+            else:
+                delta = L.act_scale[t]
+            a, b = L.step_comp(t)
+            oracle.linear(x, sid, qw, ws, inv, delta, a, b, wl.S, L.layer.abits)
+            ops += 2 * len(rows) * L.layer.K * L.layer.N
     dt = time.perf_counter() - t0
     return dict(value=ops / dt / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{len(rows)} of {M} rows through all {len(wi.layers)} linears of "
-                       f"step 0 (quantize + int32 GEMM + epilogue), {dt:.1f} s wall")
+                sample=f"{len(rows)} of {M} rows through all {len(wi.layers)} linears for "
+                       f"steps 0..{steps - 1} (quantize + int32 GEMM + epilogue), "
+                       f"{dt:.1f} s wall")
 
 
 def bf16_comparator(wl, layers, torch, reps: int = 10):
@@ -223,11 +229,12 @@ def main():
     torch.cuda.synchronize()
 
     if args.copy_bytes > 0:
+        # a plain elementwise copy kernel (reads copy_bytes, writes copy_bytes)
         src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda").fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
         for _ in range(3):
-            dst.copy_(src)
+            torch.add(src, 1, out=dst)
         torch.cuda.synchronize()
         del src, dst
 
@@ -314,7 +321,7 @@ def main():
         out["bf16_matmul_us_per_step"] = round(bf16_us, 1)
         out["speedup_vs_bf16_matmul"] = round(bf16_us / (ms_per_step * 1e3), 3)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.seed)
+        out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.cpu_steps, args.seed)
     print(json.dumps(out), flush=True)
 
 

@@ -21,6 +21,10 @@ CPU oracle on a bounded sample of the same step.
 
 --workload picks another workload (each printed as one JSON line of the
 same form, steps cycling through its step-indexed scale sets).
+--w4a4-codes picks the code container of the W4A4 linears: "int" (int4
+codes widened to int8 for the int8 matrix cores) or "e2m3" (the same 4-bit
+codes held as FP6 E2M3 for the f8f6f4 matrix cores, fp32 accumulation, exact
+for integer codes).  Outputs are identical either way.
 """
 from __future__ import annotations
 
@@ -39,6 +43,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("fused W4A8/W4A4 linear TOPS and % int8-MFMA peak; "
           "µs per denoising-step layer set")
 INT8_PEAK_TOPS = 5000.0          # MI355X dense int8 MFMA, published
+FP6_PEAK_TFLOPS = 10100.0        # MI355X dense fp6/fp4 MFMA, published
 HBM_PEAK_GBS = 8000.0            # MI355X HBM3E, published
 DEFAULT_WORKLOAD = "dit_block_h2048_m8384_16step"
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -62,6 +67,8 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--w4a4-codes", choices=["int", "e2m3"], default="int",
+                   help="code container of the W4A4 linears")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-bf16", action="store_true", help="skip the bf16 matmul comparator")
     p.add_argument("--cpu-rows", type=int, default=8384,
@@ -82,7 +89,7 @@ def _to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def prepare(wl_name: str, seed: int, torch, rudder, W):
+def prepare(wl_name: str, seed: int, torch, rudder, W, w4a4_codes: str = "int"):
     wi = W.make_inputs(wl_name, seed=seed)
     wl = wi.workload
     S = wl.S
@@ -97,8 +104,9 @@ def prepare(wl_name: str, seed: int, torch, rudder, W):
         X = xs[key]
         Wd = _to_dev_bf16(L.w, torch)
         s_d = _to_dev(L.smooth, torch)
-        Wq, ws, inv = rudder.quantize_weights(Wd, s_d)
         abits = L.layer.abits
+        codes = rudder.CODES_E2M3 if (abits == 4 and w4a4_codes == "e2m3") else rudder.CODES_INT
+        Wq, ws, inv = rudder.quantize_weights(Wd, s_d, codes)
         K, N = L.layer.K, L.layer.N
         if L.act_scale is not None:
             delta = _to_dev(L.act_scale, torch)                       # [T, S]
@@ -106,11 +114,13 @@ def prepare(wl_name: str, seed: int, torch, rudder, W):
             delta = None
         comp_a = _to_dev(L.comp_a, torch)
         comp_b = _to_dev(L.comp_b, torch)
-        Xq = torch.empty(rudder.packed_act_bytes(M, K, abits), dtype=torch.uint8, device="cuda")
+        Xq = torch.empty(rudder.packed_act_bytes(M, K, abits, codes), dtype=torch.uint8,
+                         device="cuda")
         rs = torch.empty(M, dtype=torch.float32, device="cuda")
         Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
         wsp = torch.empty(rudder.quant_act_workspace_bytes(S), dtype=torch.uint8, device="cuda")
-        layers.append(dict(name=L.layer.name, K=K, N=N, abits=abits, X=X, Wbf16=Wd, Wq=Wq,
+        layers.append(dict(name=L.layer.name, K=K, N=N, abits=abits, codes=codes, X=X,
+                           Wbf16=Wd, Wq=Wq,
                            w_scale=ws, inv=inv, delta=delta, comp_a=comp_a, comp_b=comp_b,
                            Xq=Xq, rs=rs, Y=Y, ws=wsp, src=L))
     return wi, sid_d, layers
@@ -123,21 +133,28 @@ def run_step(t: int, wl, sid_d, layers, rudder, ev=None):
     T = wl.n_steps
     tt = t % T
     for i, Ly in enumerate(layers):
-        K, N, abits = Ly["K"], Ly["N"], Ly["abits"]
+        K, N, abits, codes = Ly["K"], Ly["N"], Ly["abits"], Ly["codes"]
         if Ly["delta"] is None:
             rudder.rudder_quant_act(Ly["X"], sid_d, Ly["inv"], None, None, Ly["ws"], M, K, S,
-                                    abits, Ly["Xq"], Ly["rs"])
+                                    abits, codes, Ly["Xq"], Ly["rs"])
         else:
             rudder.rudder_quant_act(Ly["X"], sid_d, Ly["inv"], Ly["delta"][tt], None, None, M, K,
-                                    S, abits, Ly["Xq"], Ly["rs"])
+                                    S, abits, codes, Ly["Xq"], Ly["rs"])
         ca = Ly["comp_a"][tt] if Ly["comp_a"].dim() == 3 else Ly["comp_a"]
         cb = Ly["comp_b"][tt] if Ly["comp_b"].dim() == 3 else Ly["comp_b"]
         if ev is not None:
             ev[i][0].record()
         rudder.rudder_linear(Ly["Xq"], Ly["rs"], sid_d, Ly["Wq"], Ly["w_scale"], ca, cb, M, N, K,
-                             S, abits, Ly["Y"], None)
+                             S, abits, codes, Ly["Y"], None)
         if ev is not None:
             ev[i][1].record()
+
+
+def gemm_kernel_tag(Ly, rudder) -> str:
+    """One tag per GEMM kernel instance (bit width and code container)."""
+    if Ly["codes"] == rudder.CODES_E2M3:
+        return f"w4a{Ly['abits']}_e2m3_gemm"
+    return f"w4a{Ly['abits']}_gemm"
 
 
 def load_traffic(kernel_tag: str, src_hash: str):
@@ -224,7 +241,7 @@ def main():
     rudder.load_library()
     torch.cuda.set_device(0)
 
-    wi, sid_d, layers = prepare(args.workload, args.seed, torch, rudder, W)
+    wi, sid_d, layers = prepare(args.workload, args.seed, torch, rudder, W, args.w4a4_codes)
     wl = wi.workload
     torch.cuda.synchronize()
 
@@ -263,13 +280,20 @@ def main():
     for t in range(args.steps):
         for i, Ly in enumerate(layers):
             d = ev[t][i][0].elapsed_time(ev[t][i][1])
-            key = f"w4a{Ly['abits']}_gemm"
+            key = gemm_kernel_tag(Ly, rudder)
             gemm_ms.setdefault(key, []).append(d)
             gemm_ops.setdefault(key, []).append(2 * wl.M * Ly["N"] * Ly["K"])
     dominant = max(gemm_ms, key=lambda k: sum(gemm_ms[k]))
     avg_ms = float(np.mean(gemm_ms[dominant]))
     ops_per_launch = float(np.mean(gemm_ops[dominant]))
     achieved = ops_per_launch / (avg_ms * 1e-3) / 1e12
+    # a contraction is priced against the peak of the matrix-core type it runs on
+    dom_peak = FP6_PEAK_TFLOPS if "e2m3" in dominant else INT8_PEAK_TOPS
+    per_kernel = {k: {"avg_launch_us": round(float(np.mean(v)) * 1e3, 2),
+                      "launches_per_step": len(v) // args.steps,
+                      "tops": round(float(np.mean(gemm_ops[k])) / (float(np.mean(v)) * 1e-3)
+                                    / 1e12, 1)}
+                  for k, v in gemm_ms.items()}
     src_hash = kernel_source_hash()
     traffic = load_traffic(f"{dominant}_{args.workload}", src_hash)
 
@@ -297,7 +321,9 @@ def main():
             "workload": wl.name,
             "tokens": wl.M,
             "streams": {W.STREAM_NAMES[s]: int((wi.stream_id == s).sum()) for s in range(wl.S)},
-            "linears": [f"{Ly['name']} {Ly['K']}->{Ly['N']} W4A{Ly['abits']}" for Ly in layers],
+            "linears": [f"{Ly['name']} {Ly['K']}->{Ly['N']} W4A{Ly['abits']}"
+                        + (" (E2M3 codes)" if Ly["codes"] == rudder.CODES_E2M3 else "")
+                        for Ly in layers],
             "denoise_steps": wl.n_steps,
             "launches_per_step": 2 * len(layers) + (2 * len(layers) if wl.dynamic else 0),
         },
@@ -305,15 +331,16 @@ def main():
             "kernel": dominant,
             "bound": "mfma",
             "achieved": round(achieved, 2),
-            "peak": INT8_PEAK_TOPS,
+            "peak": dom_peak,
             "unit": "TFLOP/s",
-            "op_count": "2*M*N*K int8 multiply-add ops (TOPS)",
-            "frac": round(achieved / INT8_PEAK_TOPS, 4),
+            "op_count": "2*M*N*K multiply-add ops of the integer codes",
+            "frac": round(achieved / dom_peak, 4),
             "traffic": traffic,
             "avg_launch_us": round(avg_ms * 1e3, 2),
             "ops_per_launch": ops_per_launch,
             "source_hash": src_hash,
         },
+        "gemm_kernels": per_kernel,
         "wall_s": round(wall, 3),
     }
     if not args.no_bf16:

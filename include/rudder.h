@@ -59,6 +59,21 @@
  *     code 8w+i in bits 0..3 and code 8w+4+i in bits 4..7, as two's-
  *     complement nibbles; block = 512 bytes.
  * Rows from R up to the next multiple of 32 are padding and hold code 0.
+ *
+ * E2M3 container ("codes" = RUDDER_CODES_E2M3; 4-bit codes of W4A4 layers).
+ * Each code c in [-7, 7] is held as the FP6 E2M3 encoding of the integer c
+ * (bit 5 sign, bits 4..3 exponent with bias 1, bits 2..0 mantissa):
+ * |c| = 0..7 -> 0x00, 0x08, 0x10, 0x14, 0x18, 0x1A, 0x1C, 0x1E, with bit 5 set
+ * for negative c.  Every such value is exact, so the f8f6f4 matrix cores of
+ * gfx950 multiply the codes exactly and their fp32 sums stay exact integers
+ * (|sum| < 2^24 for K <= RUDDER_MAX_K).  A code matrix C[R][K] (K a multiple
+ * of 64) is cut into 32 x 64 blocks of 1536 bytes; block (rb, kb) -- rows
+ * 32rb..32rb+31, k 64kb..64kb+63 -- sits at block index rb * (K/64) + kb.
+ * Slot l = (r % 32) + 32 * ((k % 64) / 32), l = 0..63, holds the 32 codes of
+ * row r at k = 64kb + 32*(l/32) + t, t = 0..31, as a 192-bit little-endian
+ * bit string (code t in bits 6t..6t+5).  Bits 0..127 of slot l are stored at
+ * byte 16*l of the block (plane 0, 1024 bytes) and bits 128..191 at byte
+ * 1024 + 8*l (plane 1, 512 bytes).  Padding rows hold code 0.
  * ---------------------------------------------------------------------------
  */
 #ifndef RUDDER_H
@@ -78,16 +93,24 @@ typedef enum {
     RUDDER_ERR_HIP = 3            /* the HIP runtime reported a launch error */
 } rudder_status_t;
 
+/* Code containers of the packed weight and activation codes. */
+typedef enum {
+    RUDDER_CODES_INT = 0,   /* int4 split-nibble words / int8 bytes; int8 matrix cores */
+    RUDDER_CODES_E2M3 = 1   /* 4-bit codes held as FP6 E2M3 (W4A4 only); f8f6f4 matrix cores */
+} rudder_codes_t;
+
 #define RUDDER_MAX_STREAMS 8      /* S, the number of token streams, is 1..8 */
 #define RUDDER_MAX_K 65536        /* keeps every scaled int32 accumulator exact */
 
-/* Bytes of packed weight codes for a K x N layer (K, N multiples of 32):
- * N * K / 2.  Returns 0 for invalid sizes. */
-size_t rudder_packed_weight_bytes(int K, int N);
+/* Bytes of packed weight codes for a K x N layer: N * K / 2 (RUDDER_CODES_INT;
+ * K, N multiples of 32) or N * K * 3 / 4 (RUDDER_CODES_E2M3; K a multiple of
+ * 64, N of 32).  Returns 0 for invalid sizes. */
+size_t rudder_packed_weight_bytes(int K, int N, int codes);
 
 /* Bytes of activation codes for M rows (rounded up to 32) of K channels:
- * ceil(M/32)*32 * K * abits / 8.  Returns 0 for invalid sizes. */
-size_t rudder_packed_act_bytes(int M, int K, int abits);
+ * ceil(M/32)*32 * K * abits / 8 (RUDDER_CODES_INT), or ceil(M/32)*32 * K * 3/4
+ * (RUDDER_CODES_E2M3, abits = 4, K a multiple of 64).  0 for invalid sizes. */
+size_t rudder_packed_act_bytes(int M, int K, int abits, int codes);
 
 /* Bytes of device workspace rudder_quant_act needs in dynamic mode. */
 size_t rudder_quant_act_workspace_bytes(int S);
@@ -99,19 +122,21 @@ size_t rudder_quant_act_workspace_bytes(int S);
  *
  *   W          bf16 bits [K][N], row-major (input channel k, output channel n)
  *   smooth     fp32 [K], s[k] > 0
- *   K, N       > 0, multiples of 32
- *   Wq         out: rudder_packed_weight_bytes(K, N) bytes, 4-bit MFMA-tiled
+ *   K, N       > 0, multiples of 32 (K a multiple of 64 for RUDDER_CODES_E2M3)
+ *   codes      container of Wq: RUDDER_CODES_INT (any layer) or
+ *              RUDDER_CODES_E2M3 (only for W4A4 layers run with that container)
+ *   Wq         out: rudder_packed_weight_bytes(K, N, codes) bytes, MFMA-tiled
  *              layout with R = N (row = output channel)
  *   w_scale    out: fp32 [N]
  *   inv_smooth out: fp32 [K] = fl32(1 / s[k]), formed in fp64; this is what
  *              rudder_quant_act takes for the same layer
  * Errors: INVALID_ARG for a null pointer, K or N <= 0, K or N not a multiple
- * of 32, Wq/smooth/w_scale/inv_smooth not 16-byte aligned; UNSUPPORTED for
- * K > RUDDER_MAX_K.
+ * of 32 (K of 64 for E2M3), an unknown container, Wq/smooth/w_scale/
+ * inv_smooth not 16-byte aligned; UNSUPPORTED for K > RUDDER_MAX_K.
  */
 rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
-                                        uint8_t* Wq, float* w_scale, float* inv_smooth,
-                                        void* stream);
+                                        int codes, uint8_t* Wq, float* w_scale,
+                                        float* inv_smooth, void* stream);
 
 /*
  * Fused activation quantization (SteerQuant §4.4: scaling and stream gains
@@ -131,12 +156,15 @@ rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, 
  *              device scratch; ignored (may be NULL) in static mode
  *   M >= 0 (M = 0 is a no-op), K > 0 multiple of 32, 1 <= S <= 8,
  *   abits in {4, 8}
- *   Xq         out: rudder_packed_act_bytes(M, K, abits) bytes, MFMA-tiled
- *              layout with R = M (8-bit or 4-bit codes); padding rows are 0
+ *   codes      container of Xq: RUDDER_CODES_INT, or RUDDER_CODES_E2M3 (abits
+ *              = 4, K a multiple of 64)
+ *   Xq         out: rudder_packed_act_bytes(M, K, abits, codes) bytes,
+ *              MFMA-tiled layout with R = M; padding rows are 0
  *   row_scale  out: fp32 [M], row_scale[m] = D[stream_id[m]]
  * Errors: INVALID_ARG for null X/stream_id/inv_smooth/Xq/row_scale, a null
  * workspace in dynamic mode, M < 0, K <= 0, K % 32 != 0, S outside 1..8,
- * abits not 4 or 8, X/inv_smooth/Xq/workspace not 16-byte aligned;
+ * abits not 4 or 8, an unknown container or E2M3 with abits = 8 or
+ * K % 64 != 0, X/inv_smooth/Xq/workspace not 16-byte aligned;
  * UNSUPPORTED for K > RUDDER_MAX_K.
  * Dynamic mode enqueues three kernels (partial absmax, finalize, quantize);
  * static mode one.
@@ -144,7 +172,7 @@ rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, 
 rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
                                  const float* inv_smooth, const float* act_scale,
                                  float* act_scale_out, void* workspace,
-                                 int M, int K, int S, int abits,
+                                 int M, int K, int S, int abits, int codes,
                                  void* Xq, float* row_scale, void* stream);
 
 /*
@@ -152,8 +180,12 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
  * dequantization, inverse-gain compensation and bias; §1: Rudder fuses the
  * output compensation into the low-bit kernel).
  *
- *   Xq, row_scale, stream_id   from rudder_quant_act (same M, K, abits)
- *   Wq, w_scale                from rudder_quantize_weights (same K, N)
+ *   Xq, row_scale, stream_id   from rudder_quant_act (same M, K, abits, codes)
+ *   Wq, w_scale                from rudder_quantize_weights (same K, N, codes)
+ *   codes      RUDDER_CODES_INT: int4 weights widened to int8 in registers
+ *              feed int8 MFMA with int32 accumulation; RUDDER_CODES_E2M3
+ *              (abits = 4): E2M3-held 4-bit codes feed the f8f6f4 MFMA with
+ *              fp32 accumulation, exact for these integer operands
  *   comp_a, comp_b  fp32 [S][N]: the compensation of this (layer, step);
  *              y = a * t + b as one fp32 fma, the layer bias folded into b
  *   M >= 0 (M = 0 is a no-op), N > 0 multiple of 32, K > 0 multiple of 128,
@@ -162,14 +194,14 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
  *   acc_out    optional out: int32 [M][N] row-major raw accumulators
  *              sum_k qa*qw (a verification aid; pass NULL on the hot path)
  * Errors: INVALID_ARG for a null required pointer, M < 0, N or K <= 0,
- * N % 32 != 0, S outside 1..8, abits not 4 or 8, Xq/Wq/w_scale/comp_a/
- * comp_b/Y/acc_out not 16-byte aligned; UNSUPPORTED for K % 128 != 0 or
- * K > RUDDER_MAX_K.
+ * N % 32 != 0, S outside 1..8, abits not 4 or 8, an unknown container or
+ * E2M3 with abits = 8, Xq/Wq/w_scale/comp_a/comp_b/Y/acc_out not 16-byte
+ * aligned; UNSUPPORTED for K % 128 != 0 or K > RUDDER_MAX_K.
  */
 rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint8_t* stream_id,
                               const uint8_t* Wq, const float* w_scale,
                               const float* comp_a, const float* comp_b,
-                              int M, int N, int K, int S, int abits,
+                              int M, int N, int K, int S, int abits, int codes,
                               uint16_t* Y, int32_t* acc_out, void* stream);
 
 /* Static string naming a status code. */

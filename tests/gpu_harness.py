@@ -8,7 +8,16 @@ from typing import Dict, Optional
 import numpy as np
 
 import oracle
-from tiled_layout import tile_codes
+from tiled_layout import tile_codes, tile_codes_e2m3
+
+CODES_INT, CODES_E2M3 = 0, 1
+
+
+def tile_for(codes_kind: int, codes: np.ndarray, bits: int) -> np.ndarray:
+    """Oracle codes -> the byte layout the library writes for that container."""
+    if codes_kind == CODES_E2M3:
+        return tile_codes_e2m3(codes)
+    return tile_codes(codes, bits)
 
 
 def log(msg: str) -> None:
@@ -72,14 +81,15 @@ def assert_y_close(name: str, got: np.ndarray, want: np.ndarray, max_ulp: int = 
 class LayerRun:
     """One linear layer prepared on both sides (weights quantized once)."""
 
-    def __init__(self, x_bits, stream_id, w_bits, smooth, comp_a, comp_b, S, abits):
+    def __init__(self, x_bits, stream_id, w_bits, smooth, comp_a, comp_b, S, abits,
+                 codes=CODES_INT):
         from w4a4_quantized_gemm_rudder_amd import rudder
         import torch
         self.r = rudder
         self.torch = torch
         self.x_bits, self.sid, self.w_bits = x_bits, stream_id, w_bits
         self.smooth, self.comp_a, self.comp_b = smooth, comp_a, comp_b
-        self.S, self.abits = S, abits
+        self.S, self.abits, self.codes = S, abits, codes
         self.M, self.K = x_bits.shape
         self.N = w_bits.shape[1]
         # device copies
@@ -87,7 +97,8 @@ class LayerRun:
         self.sid_d = to_dev(stream_id.astype(np.uint8))
         self.W = to_dev_bf16(w_bits)
         self.s_d = to_dev(smooth.astype(np.float32))
-        self.Wq, self.w_scale, self.inv_smooth = rudder.quantize_weights(self.W, self.s_d)
+        self.Wq, self.w_scale, self.inv_smooth = rudder.quantize_weights(self.W, self.s_d,
+                                                                         codes)
         # oracle weights
         self.o_inv = oracle.inv_smooth(smooth)
         self.o_qw, self.o_ws = oracle.quantize_weights(w_bits, smooth)
@@ -95,27 +106,29 @@ class LayerRun:
     def check_weights(self) -> None:
         assert_bits_equal("inv_smooth", self.inv_smooth.cpu().numpy(), self.o_inv)
         assert_bits_equal("w_scale", self.w_scale.cpu().numpy(), self.o_ws)
-        assert_bits_equal("Wq", self.Wq.cpu().numpy(), tile_codes(self.o_qw, 4))
+        assert_bits_equal("Wq", self.Wq.cpu().numpy(), tile_for(self.codes, self.o_qw, 4))
 
     def run_step(self, delta: Optional[np.ndarray], comp_a: np.ndarray, comp_b: np.ndarray,
                  rows: Optional[np.ndarray] = None, check_codes: bool = True,
                  label: str = "") -> Dict:
         """delta None -> dynamic mode.  rows: sampled rows for acc/Y (None = all)."""
         torch, r = self.torch, self.r
-        S, abits, M, K, N = self.S, self.abits, self.M, self.K, self.N
+        S, abits, M, K, N, codes = self.S, self.abits, self.M, self.K, self.N, self.codes
         ca, cb = to_dev(comp_a.astype(np.float32)), to_dev(comp_b.astype(np.float32))
         scale_out = None
         if delta is None:
             scale_out = torch.full((S,), -1.0, dtype=torch.float32, device="cuda")
-            Xq, rs = r.quant_act(self.X, self.sid_d, self.inv_smooth, None, S, abits,
+            Xq, rs = r.quant_act(self.X, self.sid_d, self.inv_smooth, None, S, abits, codes,
                                  act_scale_out=scale_out)
         else:
-            Xq, rs = r.quant_act(self.X, self.sid_d, self.inv_smooth, to_dev(delta), S, abits)
+            Xq, rs = r.quant_act(self.X, self.sid_d, self.inv_smooth, to_dev(delta), S, abits,
+                                 codes)
         # Y exactly as the timed path produces it (no accumulator output) ...
-        Y = r.linear(Xq, rs, self.sid_d, self.Wq, self.w_scale, ca, cb, M, N, K, S, abits)
+        Y = r.linear(Xq, rs, self.sid_d, self.Wq, self.w_scale, ca, cb, M, N, K, S, abits,
+                     codes)
         # ... and once more with the raw accumulators.
         Y2, acc = r.linear(Xq, rs, self.sid_d, self.Wq, self.w_scale, ca, cb, M, N, K, S,
-                           abits, acc_out=True)
+                           abits, codes, acc_out=True)
         torch.cuda.synchronize()
 
         # oracle
@@ -127,7 +140,7 @@ class LayerRun:
         qa, o_rs = oracle.quant_act(self.x_bits, self.sid, self.o_inv, o_delta, S, abits)
         assert_bits_equal(f"{label} row_scale", rs.cpu().numpy()[:M], o_rs)
         if check_codes:
-            assert_bits_equal(f"{label} Xq", Xq.cpu().numpy(), tile_codes(qa, abits))
+            assert_bits_equal(f"{label} Xq", Xq.cpu().numpy(), tile_for(codes, qa, abits))
         if rows is None:
             rows = np.arange(M)
         o_acc = oracle.int_gemm(np.ascontiguousarray(qa[rows]), self.o_qw)

@@ -8,7 +8,8 @@ import re
 import numpy as np
 import pytest
 
-from tiled_layout import tile_codes, untile_codes
+from tiled_layout import (E2M3_OF, e2m3_value, tile_codes, tile_codes_e2m3, untile_codes,
+                          untile_codes_e2m3)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -43,6 +44,14 @@ def test_size_helpers(lib):
     assert r.packed_act_bytes(0, 128, 8) == 0
     assert r.packed_act_bytes(10, 128, 5) == 0
     assert r.quant_act_workspace_bytes(3) >= 4 * 8 * 2
+    # E2M3 container: 6 bits per code, K a multiple of 64, W4A4 only
+    E = r.CODES_E2M3
+    assert r.packed_weight_bytes(2048, 6144, E) == 2048 * 6144 * 3 // 4
+    assert r.packed_weight_bytes(96, 64, E) == 0
+    assert r.packed_act_bytes(4192, 2048, 4, E) == 4192 * 2048 * 3 // 4
+    assert r.packed_act_bytes(1, 128, 4, E) == 32 * 128 * 3 // 4
+    assert r.packed_act_bytes(64, 128, 8, E) == 0
+    assert r.packed_weight_bytes(128, 64, 7) == 0
 
 
 def test_status_strings(lib):
@@ -60,11 +69,11 @@ P = 0x1000
 
 def _linear(lib, **kw):
     args = dict(Xq=P, rs=P, sid=P, Wq=P, ws=P, a=P, b=P, M=64, N=256, K=256, S=3, abits=8,
-                Y=P, acc=None)
+                codes=0, Y=P, acc=None)
     args.update(kw)
     return lib.rudder_linear(args["Xq"], args["rs"], args["sid"], args["Wq"], args["ws"],
                              args["a"], args["b"], args["M"], args["N"], args["K"], args["S"],
-                             args["abits"], args["Y"], args["acc"], None)
+                             args["abits"], args["codes"], args["Y"], args["acc"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -73,6 +82,8 @@ def _linear(lib, **kw):
     (dict(M=-1), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(N=48), 1),
     (dict(S=0), 1), (dict(S=9), 1), (dict(abits=5), 1), (dict(abits=16), 1),
     (dict(K=96), 2), (dict(K=65536 + 128), 2),
+    (dict(codes=2), 1), (dict(codes=-1), 1), (dict(codes=1, abits=8), 1),
+    (dict(codes=1, abits=4, K=96), 2),
 ])
 def test_linear_rejects(lib, kw, status):
     assert _linear(lib, **kw) == status
@@ -86,11 +97,11 @@ def test_linear_m0_is_noop(lib):
 
 def _quant_act(lib, **kw):
     args = dict(X=P, sid=P, inv=P, scale=P, out=None, ws=None, M=64, K=256, S=3, abits=8,
-                Xq=P, rs=P)
+                codes=0, Xq=P, rs=P)
     args.update(kw)
     return lib.rudder_quant_act(args["X"], args["sid"], args["inv"], args["scale"], args["out"],
                                 args["ws"], args["M"], args["K"], args["S"], args["abits"],
-                                args["Xq"], args["rs"], None)
+                                args["codes"], args["Xq"], args["rs"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -98,6 +109,7 @@ def _quant_act(lib, **kw):
     (dict(rs=None), 1), (dict(scale=None, ws=None), 1),
     (dict(M=-5), 1), (dict(K=0), 1), (dict(K=48), 1), (dict(S=0), 1), (dict(S=9), 1),
     (dict(abits=2), 1), (dict(K=65536 + 32), 2),
+    (dict(codes=3), 1), (dict(codes=1), 1), (dict(codes=1, abits=4, K=96), 1),
 ])
 def test_quant_act_rejects(lib, kw, status):
     assert _quant_act(lib, **kw) == status
@@ -109,19 +121,20 @@ def test_quant_act_m0_is_noop(lib):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(W=None), 1), (dict(K=0), 1), (dict(N=-32), 1), (dict(K=40), 1), (dict(N=40), 1),
-    (dict(K=65536 + 32), 2),
+    (dict(K=65536 + 32), 2), (dict(codes=5), 1), (dict(codes=1, K=96), 1),
 ])
 def test_quantize_weights_rejects(lib, kw, status):
-    args = dict(W=P, s=P, K=256, N=256, Wq=P, ws=P, inv=P)
+    args = dict(W=P, s=P, K=256, N=256, codes=0, Wq=P, ws=P, inv=P)
     args.update(kw)
-    assert lib.rudder_quantize_weights(args["W"], args["s"], args["K"], args["N"], args["Wq"],
-                                       args["ws"], args["inv"], None) == status
+    assert lib.rudder_quantize_weights(args["W"], args["s"], args["K"], args["N"],
+                                       args["codes"], args["Wq"], args["ws"], args["inv"],
+                                       None) == status
 
 
 def test_binding_raises_with_message(lib):
     from w4a4_quantized_gemm_rudder_amd import rudder
     with pytest.raises(rudder.RudderError) as ei:
-        rudder.rudder_linear(P, P, P, P, P, P, P, 64, 256, 96, 3, 8, P, None, stream=0)
+        rudder.rudder_linear(P, P, P, P, P, P, P, 64, 256, 96, 3, 8, 0, P, None, stream=0)
     assert ei.value.status == rudder.RUDDER_ERR_UNSUPPORTED
     assert "K=96" in str(ei.value)
 
@@ -149,6 +162,34 @@ def test_tiled_layout_roundtrip_and_slots(bits):
         b = buf[base:base + 8]
         assert (b[0] & 0xF) == (codes[0] & 0xF) and (b[0] >> 4) == (codes[4] & 0xF)
         assert (b[5] & 0xF) == (codes[9] & 0xF) and (b[5] >> 4) == (codes[13] & 0xF)
+
+
+def test_e2m3_layout_roundtrip_and_slots():
+    """Test-side E2M3 tiler against the header's definition, checked by hand on
+    one slot, and the E2M3 decode against the format's own rule."""
+    # every integer code 0..7 is exact in E2M3 and its encoding decodes back
+    for v, enc in E2M3_OF.items():
+        assert e2m3_value(np.array([enc]))[0] == v
+        assert e2m3_value(np.array([enc | 0x20]))[0] == -v
+    # largest finite E2M3 magnitude is 7.5 (e=3, m=7); subnormal step 1/8
+    assert e2m3_value(np.array([0x1F]))[0] == 7.5
+    assert e2m3_value(np.array([0x01]))[0] == 0.125
+    rng = np.random.default_rng(1)
+    R, K = 45, 192
+    c = rng.integers(-7, 8, (R, K)).astype(np.int8)
+    buf = tile_codes_e2m3(c)
+    assert buf.size == 64 * K * 3 // 4
+    back = untile_codes_e2m3(buf, R, K)
+    assert np.array_equal(back[:R], c) and np.all(back[R:] == 0)
+    # row 37, k = 64*2 + 32 + t  ->  block 1*3+2, slot 5+32
+    blk = (1 * (K // 64) + 2) * 1536
+    slot = 5 + 32
+    p0 = buf[blk + 16 * slot: blk + 16 * slot + 16]
+    p1 = buf[blk + 1024 + 8 * slot: blk + 1024 + 8 * slot + 8]
+    bits = int.from_bytes(bytes(p0) + bytes(p1), "little")
+    for t in range(32):
+        field = (bits >> (6 * t)) & 0x3F
+        assert e2m3_value(np.array([field]))[0] == c[37, 160 + t]
 
 
 def test_misaligned_rejected(lib):

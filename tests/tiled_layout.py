@@ -59,3 +59,69 @@ def untile_codes(buf: np.ndarray, R: int, K: int, bits: int) -> np.ndarray:
         t = np.concatenate([lo, hi], axis=-1).reshape(Rp // 32, K // 32, 2, 32, 16)
         t = t.astype(np.int8)
     return np.ascontiguousarray(t.transpose(0, 3, 1, 2, 4)).reshape(Rp, K)
+
+
+# ---------------------------------------------------------------------------
+# E2M3 container (definition in include/rudder.h): each code c in [-7, 7] is
+# the 6-bit FP6 E2M3 encoding of the integer c; 32 x 64 blocks of 1536 bytes;
+# slot l = (r%32) + 32*((k%64)//32) holds 32 codes as a 192-bit little-endian
+# string (code t at bits 6t..6t+5): bits 0..127 at byte 16*l (plane 0), bits
+# 128..191 at byte 1024 + 8*l (plane 1).
+# ---------------------------------------------------------------------------
+E2M3_OF = {0: 0x00, 1: 0x08, 2: 0x10, 3: 0x14, 4: 0x18, 5: 0x1A, 6: 0x1C, 7: 0x1E}
+
+
+def e2m3_value(code6: np.ndarray) -> np.ndarray:
+    """Decode 6-bit E2M3 fields to floats straight from the format (sign,
+    2-bit exponent with bias 1, 3-bit mantissa, subnormals at exponent 0)."""
+    c = np.asarray(code6, np.int64)
+    sign = np.where(c & 0x20, -1.0, 1.0)
+    e = (c >> 3) & 0x3
+    m = c & 0x7
+    mag = np.where(e == 0, m / 8.0, (1.0 + m / 8.0) * 2.0 ** (e - 1))
+    return sign * mag
+
+
+def tile_codes_e2m3(codes: np.ndarray) -> np.ndarray:
+    codes = _pad_rows(np.asarray(codes, np.int8))
+    Rp, K = codes.shape
+    assert K % 64 == 0
+    enc = np.vectorize(lambda v: E2M3_OF[abs(int(v))] | (0x20 if v < 0 else 0))(codes)
+    enc = enc.astype(np.uint64)
+    # [rb, r32, kb, half, t] -> [rb, kb, half, r32, t]
+    t = enc.reshape(Rp // 32, 32, K // 64, 2, 32).transpose(0, 2, 3, 1, 4)
+    # assemble 192-bit strings as three 64-bit words
+    words = np.zeros(t.shape[:-1] + (3,), np.uint64)
+    for ti in range(32):
+        bit = 6 * ti
+        w, off = bit // 64, bit % 64
+        words[..., w] |= t[..., ti] << np.uint64(off)
+        if off > 58:
+            words[..., w + 1] |= t[..., ti] >> np.uint64(64 - off)
+    b = words.view(np.uint8).reshape(t.shape[:-1] + (24,))      # [rb, kb, half, r32, 24]
+    b = b.reshape(Rp // 32, K // 64, 64, 24)                      # slot = r32 + 32*half
+    out = np.concatenate([b[..., :16].reshape(Rp // 32, K // 64, 1024),
+                          b[..., 16:].reshape(Rp // 32, K // 64, 512)], axis=-1)
+    return np.ascontiguousarray(out).reshape(-1)
+
+
+def untile_codes_e2m3(buf: np.ndarray, R: int, K: int) -> np.ndarray:
+    Rp = (R + 31) // 32 * 32
+    blk = np.asarray(buf, np.uint8).reshape(-1)[: Rp * K * 3 // 4].reshape(Rp // 32, K // 64,
+                                                                             1536)
+    p0 = blk[..., :1024].reshape(Rp // 32, K // 64, 64, 16)
+    p1 = blk[..., 1024:].reshape(Rp // 32, K // 64, 64, 8)
+    b = np.concatenate([p0, p1], axis=-1)                          # [rb, kb, slot, 24]
+    words = np.ascontiguousarray(b).view(np.uint64)                # [rb, kb, slot, 3]
+    vals = np.zeros(b.shape[:-1] + (32,), np.int64)
+    for ti in range(32):
+        bit = 6 * ti
+        w, off = bit // 64, bit % 64
+        v = words[..., w] >> np.uint64(off)
+        if off > 58:
+            v |= words[..., w + 1] << np.uint64(64 - off)
+        vals[..., ti] = (v & np.uint64(0x3F)).astype(np.int64)
+    dec = e2m3_value(vals)
+    assert np.all(dec == np.round(dec)) and np.all(np.abs(dec) <= 7.5)
+    codes = dec.astype(np.int8).reshape(Rp // 32, K // 64, 2, 32, 32)   # [rb, kb, half, r32, t]
+    return np.ascontiguousarray(codes.transpose(0, 3, 1, 2, 4)).reshape(Rp, K)

@@ -22,6 +22,7 @@ constexpr int kMaxPartials = 1024;          // dynamic-mode partial-absmax block
 // ---------------------------------------------------------------------------
 // Weight preparation: one block per 32 output channels.
 // ---------------------------------------------------------------------------
+template <int CODES>
 __global__ __launch_bounds__(kThreads) void quantize_weights_kernel(
     const uint16_t* __restrict__ W, const float* __restrict__ smooth, int K, int N,
     uint8_t* __restrict__ Wq, float* __restrict__ w_scale, float* __restrict__ inv_smooth) {
@@ -55,24 +56,34 @@ __global__ __launch_bounds__(kThreads) void quantize_weights_kernel(
     }
     __syncthreads();
 
-    // Codes: slot q -> (channel n0 + q % 32, 16 k starting at 16 * (q / 32)).
-    const int slots = 32 * (K / 16);
+    // Codes: slot q -> (channel n0 + q % 32, kSlot k starting at kSlot * (q / 32)).
+    constexpr int kSlot = CODES == RUDDER_CODES_E2M3 ? 32 : 16;
+    const int slots = 32 * (K / kSlot);
     for (int q = tid; q < slots; q += kThreads) {
         const int jj = q & 31;
         const int nn = blockIdx.x * 32 + jj;
-        const int k0 = 16 * (q >> 5);
+        const int k0 = kSlot * (q >> 5);
         const float iw = s_inv_w[jj];
-        int c[16];
+        int c[kSlot];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
+        for (int i = 0; i < kSlot; ++i) {
             const int k = k0 + i;
             float w = bf16_bits_to_float(W[(size_t)k * N + nn]) * smooth[k];
             c[i] = quantize_clamped(w * iw, 7.0f);
         }
-        uint2 out;
-        out.x = split_nibble_word(c);
-        out.y = split_nibble_word(c + 8);
-        *reinterpret_cast<uint2*>(Wq + tiled_slot_offset<4>(nn, k0, K)) = out;
+        if constexpr (CODES == RUDDER_CODES_E2M3) {
+            uint32_t d[6];
+            pack_e2m3x32(c, d);
+            uint8_t* blk = Wq + e2m3_block_offset(nn, k0, K);
+            const int slot = e2m3_slot(nn, k0);
+            *reinterpret_cast<uint4*>(blk + slot * 16) = make_uint4(d[0], d[1], d[2], d[3]);
+            *reinterpret_cast<uint2*>(blk + 1024 + slot * 8) = make_uint2(d[4], d[5]);
+        } else {
+            uint2 out;
+            out.x = split_nibble_word(c);
+            out.y = split_nibble_word(c + 8);
+            *reinterpret_cast<uint2*>(Wq + tiled_slot_offset<4>(nn, k0, K)) = out;
+        }
     }
 }
 
@@ -143,6 +154,70 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
         out.y = split_nibble_word(c + 8);
         *reinterpret_cast<uint2*>(Xq + tiled_slot_offset<4>(r, k0, K)) = out;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Activation quantizer, E2M3 container (4-bit codes).  One wave per 32 x 64
+// (row, k) block: lane l handles row 32rb + l % 32 and the 32 k starting at
+// 64kb + 32 (l / 32); plane 0 and plane 1 of the block are each written
+// contiguously by the wave.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
+    const uint16_t* __restrict__ X, const uint8_t* __restrict__ sid,
+    const float* __restrict__ inv_smooth, const float* __restrict__ delta, int M, int K, int S,
+    uint8_t* __restrict__ Xq, float* __restrict__ row_scale) {
+    __shared__ float s_delta[RUDDER_MAX_STREAMS];
+    __shared__ float s_ia[RUDDER_MAX_STREAMS];
+    const int tid = threadIdx.x;
+    if (tid < RUDDER_MAX_STREAMS) {
+        float d = tid < S ? delta[tid] : 0.0f;
+        s_delta[tid] = d;
+        s_ia[tid] = step_reciprocal(d);
+    }
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int kblocks = K >> 6;
+    const int total = ((M + 31) >> 5) * kblocks;
+    const int gw = blockIdx.x * (kThreads / 64) + (tid >> 6);
+    if (gw >= total) return;
+    const int rb = gw / kblocks;
+    const int kb = gw - rb * kblocks;
+    const int r = rb * 32 + (lane & 31);
+    const int k0 = kb * 64 + 32 * (lane >> 5);
+
+    int c[32];
+    if (r < M) {
+        const int s = sid[r] & (RUDDER_MAX_STREAMS - 1);
+        const float ia = s_ia[s];
+        const uint4* xp = reinterpret_cast<const uint4*>(X + (size_t)r * K + k0);
+        const float4* sp = reinterpret_cast<const float4*>(inv_smooth + k0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 x0 = xp[2 * h], x1 = xp[2 * h + 1];
+            const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+            const float4 s0 = sp[4 * h], s1 = sp[4 * h + 1], s2 = sp[4 * h + 2],
+                         s3 = sp[4 * h + 3];
+            const float is[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
+                                  s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const uint32_t hbits = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
+                const float u = bf16_bits_to_float(hbits) * is[i];
+                c[16 * h + i] = quantize_clamped(u * ia, 7.0f);
+            }
+        }
+        if (kb == 0 && lane < 32) row_scale[r] = s_delta[s];
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) c[i] = 0;
+    }
+    uint32_t d[6];
+    pack_e2m3x32(c, d);
+    uint8_t* blk = Xq + e2m3_block_offset(r, k0, K);
+    const int slot = e2m3_slot(r, k0);
+    *reinterpret_cast<uint4*>(blk + slot * 16) = make_uint4(d[0], d[1], d[2], d[3]);
+    *reinterpret_cast<uint2*>(blk + 1024 + slot * 8) = make_uint2(d[4], d[5]);
 }
 
 // ---------------------------------------------------------------------------
@@ -232,16 +307,27 @@ size_t quant_act_workspace_bytes() {
 }
 
 hipError_t launch_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
-                                   uint8_t* Wq, float* w_scale, float* inv_smooth,
+                                   int codes, uint8_t* Wq, float* w_scale, float* inv_smooth,
                                    hipStream_t stream) {
-    hipLaunchKernelGGL(quantize_weights_kernel, dim3(N / 32), dim3(kThreads), 0, stream, W,
-                       smooth, K, N, Wq, w_scale, inv_smooth);
+    if (codes == RUDDER_CODES_E2M3)
+        hipLaunchKernelGGL(quantize_weights_kernel<RUDDER_CODES_E2M3>, dim3(N / 32),
+                           dim3(kThreads), 0, stream, W, smooth, K, N, Wq, w_scale, inv_smooth);
+    else
+        hipLaunchKernelGGL(quantize_weights_kernel<RUDDER_CODES_INT>, dim3(N / 32),
+                           dim3(kThreads), 0, stream, W, smooth, K, N, Wq, w_scale, inv_smooth);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_act_static(const uint16_t* X, const uint8_t* sid, const float* inv_smooth,
-                                   const float* delta, int M, int K, int S, int abits, void* Xq,
-                                   float* row_scale, hipStream_t stream) {
+                                   const float* delta, int M, int K, int S, int abits, int codes,
+                                   void* Xq, float* row_scale, hipStream_t stream) {
+    if (codes == RUDDER_CODES_E2M3) {
+        const long waves = (long)((M + 31) / 32) * (K / 64);
+        hipLaunchKernelGGL(quant_act_e2m3_kernel, dim3((unsigned)((waves + 3) / 4)),
+                           dim3(kThreads), 0, stream, X, sid, inv_smooth, delta, M, K, S,
+                           static_cast<uint8_t*>(Xq), row_scale);
+        return hipGetLastError();
+    }
     const long waves = (long)((M + 31) / 32) * (K / 32);
     const dim3 grid((unsigned)((waves + 3) / 4));
     if (abits == 8)
@@ -255,8 +341,8 @@ hipError_t launch_quant_act_static(const uint16_t* X, const uint8_t* sid, const 
 
 hipError_t launch_quant_act_dynamic(const uint16_t* X, const uint8_t* sid,
                                     const float* inv_smooth, float* act_scale_out,
-                                    void* workspace, int M, int K, int S, int abits, void* Xq,
-                                    float* row_scale, hipStream_t stream) {
+                                    void* workspace, int M, int K, int S, int abits, int codes,
+                                    void* Xq, float* row_scale, hipStream_t stream) {
     float* partial = static_cast<float*>(workspace);
     float* delta = partial + (size_t)kMaxPartials * RUDDER_MAX_STREAMS;
     const long chunks = (long)M * (K / 16);
@@ -271,8 +357,8 @@ hipError_t launch_quant_act_dynamic(const uint16_t* X, const uint8_t* sid,
                        (int)nb, S, abits == 8 ? 127.0f : 7.0f, delta, act_scale_out);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    return launch_quant_act_static(X, sid, inv_smooth, delta, M, K, S, abits, Xq, row_scale,
-                                   stream);
+    return launch_quant_act_static(X, sid, inv_smooth, delta, M, K, S, abits, codes, Xq,
+                                   row_scale, stream);
 }
 
 }  // namespace rudder

@@ -40,15 +40,20 @@ rudder_status_t from_hip(hipError_t e, const char* what) {
 
 extern "C" {
 
-size_t rudder_packed_weight_bytes(int K, int N) {
+size_t rudder_packed_weight_bytes(int K, int N, int codes) {
     if (K <= 0 || N <= 0 || K % 32 || N % 32) return 0;
-    return (size_t)N * (size_t)K / 2;
+    if (codes == RUDDER_CODES_INT) return (size_t)N * (size_t)K / 2;
+    if (codes == RUDDER_CODES_E2M3 && K % 64 == 0) return (size_t)N * (size_t)K * 3 / 4;
+    return 0;
 }
 
-size_t rudder_packed_act_bytes(int M, int K, int abits) {
+size_t rudder_packed_act_bytes(int M, int K, int abits, int codes) {
     if (M < 0 || K <= 0 || K % 32 || (abits != 4 && abits != 8)) return 0;
     const size_t rows = (size_t)((M + 31) / 32) * 32;
-    return rows * (size_t)K * (size_t)abits / 8;
+    if (codes == RUDDER_CODES_INT) return rows * (size_t)K * (size_t)abits / 8;
+    if (codes == RUDDER_CODES_E2M3 && abits == 4 && K % 64 == 0)
+        return rows * (size_t)K * 3 / 4;
+    return 0;
 }
 
 size_t rudder_quant_act_workspace_bytes(int S) {
@@ -57,8 +62,8 @@ size_t rudder_quant_act_workspace_bytes(int S) {
 }
 
 rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
-                                        uint8_t* Wq, float* w_scale, float* inv_smooth,
-                                        void* stream) {
+                                        int codes, uint8_t* Wq, float* w_scale,
+                                        float* inv_smooth, void* stream) {
     const char* f = "rudder_quantize_weights";
     if (!W || !smooth || !Wq || !w_scale || !inv_smooth)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
@@ -66,20 +71,26 @@ rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, 
         return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d and N=%d must be positive", f, K, N);
     if (K % 32 || N % 32)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d and N=%d must be multiples of 32", f, K, N);
+    if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
+    if (codes == RUDDER_CODES_E2M3 && K % 64)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 64 for E2M3 codes",
+                    f, K);
     if (misaligned(Wq) || misaligned(smooth) || misaligned(w_scale) || misaligned(inv_smooth))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: Wq, smooth, w_scale and inv_smooth must be "
                     "16-byte aligned", f);
     if (K > RUDDER_MAX_K)
         return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
-    return from_hip(rudder::launch_quantize_weights(W, smooth, K, N, Wq, w_scale, inv_smooth,
-                                                    static_cast<hipStream_t>(stream)),
+    return from_hip(rudder::launch_quantize_weights(W, smooth, K, N, codes, Wq, w_scale,
+                                                    inv_smooth, static_cast<hipStream_t>(stream)),
                     f);
 }
 
 rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
                                  const float* inv_smooth, const float* act_scale,
                                  float* act_scale_out, void* workspace, int M, int K, int S,
-                                 int abits, void* Xq, float* row_scale, void* stream) {
+                                 int abits, int codes, void* Xq, float* row_scale,
+                                 void* stream) {
     const char* f = "rudder_quant_act";
     if (!X || !stream_id || !inv_smooth || !Xq || !row_scale)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
@@ -93,6 +104,12 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
         return fail(RUDDER_ERR_INVALID_ARG, "%s: S=%d must be in 1..%d", f, S, RUDDER_MAX_STREAMS);
     if (abits != 4 && abits != 8)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
+    if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
+    if (codes == RUDDER_CODES_E2M3 && (abits != 4 || K % 64))
+        return fail(RUDDER_ERR_INVALID_ARG,
+                    "%s: E2M3 codes need abits=4 and K a multiple of 64 (abits=%d, K=%d)", f,
+                    abits, K);
     if (misaligned(X) || misaligned(inv_smooth) || misaligned(Xq) || misaligned(workspace))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: X, inv_smooth, Xq and workspace must be "
                     "16-byte aligned", f);
@@ -102,17 +119,18 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
     hipStream_t st = static_cast<hipStream_t>(stream);
     if (act_scale != nullptr)
         return from_hip(rudder::launch_quant_act_static(X, stream_id, inv_smooth, act_scale, M, K,
-                                                        S, abits, Xq, row_scale, st),
+                                                        S, abits, codes, Xq, row_scale, st),
                         f);
     return from_hip(rudder::launch_quant_act_dynamic(X, stream_id, inv_smooth, act_scale_out,
-                                                     workspace, M, K, S, abits, Xq, row_scale, st),
+                                                     workspace, M, K, S, abits, codes, Xq,
+                                                     row_scale, st),
                     f);
 }
 
 rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint8_t* stream_id,
                               const uint8_t* Wq, const float* w_scale, const float* comp_a,
                               const float* comp_b, int M, int N, int K, int S, int abits,
-                              uint16_t* Y, int32_t* acc_out, void* stream) {
+                              int codes, uint16_t* Y, int32_t* acc_out, void* stream) {
     const char* f = "rudder_linear";
     if (!Xq || !row_scale || !stream_id || !Wq || !w_scale || !comp_a || !comp_b || !Y)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
@@ -124,6 +142,10 @@ rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint
         return fail(RUDDER_ERR_INVALID_ARG, "%s: S=%d must be in 1..%d", f, S, RUDDER_MAX_STREAMS);
     if (abits != 4 && abits != 8)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
+    if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
+    if (codes == RUDDER_CODES_E2M3 && abits != 4)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: E2M3 codes need abits=4 (abits=%d)", f, abits);
     if (misaligned(Xq) || misaligned(Wq) || misaligned(w_scale) || misaligned(comp_a) ||
         misaligned(comp_b) || misaligned(Y) || misaligned(acc_out))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: Xq, Wq, w_scale, comp_a, comp_b, Y and acc_out "
@@ -134,7 +156,7 @@ rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint
         return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
     if (M == 0) return ok();
     return from_hip(rudder::launch_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b,
-                                          M, N, K, S, abits, Y, acc_out,
+                                          M, N, K, S, abits, codes, Y, acc_out,
                                           static_cast<hipStream_t>(stream)),
                     f);
 }

@@ -14,24 +14,24 @@ namespace rudder {
 // validated by the C ABI layer; each returns the launch's hipError_t.
 // ---------------------------------------------------------------------------
 hipError_t launch_quantize_weights(const uint16_t* W, const float* smooth, int K, int N,
-                                   uint8_t* Wq, float* w_scale, float* inv_smooth,
+                                   int codes, uint8_t* Wq, float* w_scale, float* inv_smooth,
                                    hipStream_t stream);
 
 hipError_t launch_quant_act_static(const uint16_t* X, const uint8_t* sid, const float* inv_smooth,
-                                   const float* delta, int M, int K, int S, int abits, void* Xq,
-                                   float* row_scale, hipStream_t stream);
+                                   const float* delta, int M, int K, int S, int abits, int codes,
+                                   void* Xq, float* row_scale, hipStream_t stream);
 
 hipError_t launch_quant_act_dynamic(const uint16_t* X, const uint8_t* sid,
                                     const float* inv_smooth, float* act_scale_out,
-                                    void* workspace, int M, int K, int S, int abits, void* Xq,
-                                    float* row_scale, hipStream_t stream);
+                                    void* workspace, int M, int K, int S, int abits, int codes,
+                                    void* Xq, float* row_scale, hipStream_t stream);
 
 size_t quant_act_workspace_bytes();
 
 hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* sid,
                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
-                         const float* comp_b, int M, int N, int K, int S, int abits, uint16_t* Y,
-                         int32_t* acc_out, hipStream_t stream);
+                         const float* comp_b, int M, int N, int K, int S, int abits, int codes,
+                         uint16_t* Y, int32_t* acc_out, hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers
@@ -87,5 +87,35 @@ __device__ __forceinline__ size_t tiled_slot_offset(int r, int k, int K) {
     int slot = (r & 31) + 32 * ((k & 31) >> 4);
     return block * BLOCK_BYTES + (size_t)slot * SLOT_BYTES;
 }
+
+// FP6 E2M3 encoding of an integer code c in [-7, 7] (6 bits: sign in bit 5,
+// exponent bias 1 in bits 4..3, mantissa in bits 2..0).
+__device__ __forceinline__ uint32_t e2m3_code(int c) {
+    const uint32_t a = (uint32_t)(c < 0 ? -c : c);
+    // |c| = 0..7 -> 0x00 0x08 0x10 0x14 0x18 0x1A 0x1C 0x1E
+    const uint64_t table = 0x1E1C1A1814100800ull;
+    return (uint32_t)((table >> (8 * a)) & 0x3Fu) | (c < 0 ? 0x20u : 0u);
+}
+
+// Pack 32 codes (t = 0..31) as a 192-bit little-endian string of 6-bit
+// E2M3 fields (field t at bits 6t..6t+5) into six dwords.
+__device__ __forceinline__ void pack_e2m3x32(const int* c, uint32_t (&d)[6]) {
+#pragma unroll
+    for (int i = 0; i < 6; ++i) d[i] = 0;
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+        const uint32_t v = e2m3_code(c[t]);
+        const int bit = 6 * t;
+        d[bit >> 5] |= v << (bit & 31);
+        if ((bit & 31) > 26) d[(bit >> 5) + 1] |= v >> (32 - (bit & 31));
+    }
+}
+
+// Byte offsets of slot (row r, k) in an E2M3 code matrix with K columns:
+// plane 0 (16 bytes) and plane 1 (8 bytes) of the 1536-byte 32 x 64 block.
+__device__ __forceinline__ size_t e2m3_block_offset(int r, int k, int K) {
+    return ((size_t)(r >> 5) * (size_t)(K >> 6) + (size_t)(k >> 6)) * 1536;
+}
+__device__ __forceinline__ int e2m3_slot(int r, int k) { return (r & 31) + 32 * ((k & 63) >> 5); }
 
 }  // namespace rudder

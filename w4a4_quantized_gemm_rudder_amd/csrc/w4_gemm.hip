@@ -25,6 +25,11 @@
 //   * Epilogue: dequantize + compensate in registers, stage the bf16 tile in
 //     LDS (XOR-swizzled 16-byte chunks), then store whole 512-byte row
 //     segments with 16-byte stores so every HBM line is written once.
+//   * E2M3 container (W4A4): 4-bit codes held as FP6 E2M3 feed
+//     v_mfma_scale_f32_32x32x64_f8f6f4 directly (unit scales): no widening, and
+//     twice the int8 rate.  Products of codes are small integers and every
+//     fp32 partial sum is an integer below 2^24, so the fp32 accumulator holds
+//     the exact integer dot product.
 //   * Tile order: workgroups are dealt round-robin to the 8 XCDs; the grid is
 //     remapped so each XCD walks a contiguous, m-grouped range of tiles and
 //     the tiles in flight on one XCD share activation and weight panels in
@@ -37,7 +42,9 @@ namespace rudder {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BM = 128;          // tokens per block tile
@@ -51,16 +58,61 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int FW = BN / kWavesN / 32;   // 32-channel fragments per wave (2)
 constexpr int FA = BM / kWavesM / 32;   // 32-token fragments per wave (4)
 constexpr int kXcds = 8;
-constexpr int kGroupM = 4;       // m-tiles per tile group (L2 reuse of weight panels)
+constexpr int kGroupM = 8;       // m-tiles per tile group (L2 reuse of weight panels)
 
-template <int ABITS, int NS>
-struct Cfg {
-    static constexpr int kActBlock = 64 * 2 * ABITS;                 // 1024 / 512 bytes
-    static constexpr int kActPerMb = (BK / 32) * kActBlock;          // per 32-token block
-    static constexpr int kActBytes = (BM / 32) * kActPerMb;          // 32 / 16 KiB
+// Code formats of the GEMM.
+constexpr int kFmtA8 = 0;        // int8 activations, int4 weights (int8 MFMA)
+constexpr int kFmtA4 = 1;        // int4 activations and weights (int8 MFMA)
+constexpr int kFmtF6 = 2;        // 4-bit codes held as E2M3 (f8f6f4 MFMA)
+
+// Six dwords of one E2M3 fragment (plane 0: 16 bytes, plane 1: 8 bytes).
+struct F6Frag {
+    uint4 p0;
+    uint2 p1;
+};
+
+template <int FMT>
+struct Fmt;
+template <>
+struct Fmt<kFmtA8> {
+    static constexpr int kKSub = 32;       // k per MFMA
+    static constexpr int kABlock = 1024;   // bytes per 32-row x kKSub code block
     static constexpr int kWBlock = 512;
-    static constexpr int kWPerNb = (BK / 32) * kWBlock;              // 2 KiB
-    static constexpr int kWBytes = (BN / 32) * kWPerNb;              // 16 KiB
+    static constexpr int kReadAhead = 2;   // substeps of fragment read-ahead
+    typedef uint2 WFrag;
+    typedef uint4 AFrag;
+    typedef v16i Acc;
+};
+template <>
+struct Fmt<kFmtA4> {
+    static constexpr int kKSub = 32;
+    static constexpr int kABlock = 512;
+    static constexpr int kWBlock = 512;
+    static constexpr int kReadAhead = 2;
+    typedef uint2 WFrag;
+    typedef uint2 AFrag;
+    typedef v16i Acc;
+};
+template <>
+struct Fmt<kFmtF6> {
+    static constexpr int kKSub = 64;
+    static constexpr int kABlock = 1536;
+    static constexpr int kWBlock = 1536;
+    static constexpr int kReadAhead = 1;
+    typedef F6Frag WFrag;
+    typedef F6Frag AFrag;
+    typedef v16f Acc;
+};
+
+template <int FMT, int NS>
+struct Cfg {
+    using F = Fmt<FMT>;
+    static constexpr int kActBlock = F::kABlock;
+    static constexpr int kActPerMb = (BK / F::kKSub) * kActBlock;    // per 32-token block
+    static constexpr int kActBytes = (BM / 32) * kActPerMb;
+    static constexpr int kWBlock = F::kWBlock;
+    static constexpr int kWPerNb = (BK / F::kKSub) * kWBlock;        // per 32-channel block
+    static constexpr int kWBytes = (BN / 32) * kWPerNb;
     static constexpr int kStageBytes = kActBytes + kWBytes;
     static constexpr int kRingBytes = NS * kStageBytes;
     // 16-byte direct loads per thread per stage (each wave instruction = 1 KiB)
@@ -155,79 +207,103 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblk, int tiles_m, in
     tn = local / gm;
 }
 
-// Raw (still packed) fragment words of one 32-wide k-substep.
-template <int ABITS>
+// Raw (still packed) fragment words of one k-substep.
+template <int FMT>
 struct RawFrags {
-    uint2 w[FW];                                    // channel blocks x 16 nibbles
-    typename std::conditional<ABITS == 8, uint4, uint2>::type a[FA];  // token blocks
+    typename Fmt<FMT>::WFrag w[FW];                 // channel blocks
+    typename Fmt<FMT>::AFrag a[FA];                 // token blocks
 };
 
-template <int ABITS, int NS>
+template <typename T>
+__device__ __forceinline__ void read_frag(const uint8_t* block, int lane, T& out);
+template <>
+__device__ __forceinline__ void read_frag<uint2>(const uint8_t* block, int lane, uint2& out) {
+    out = *reinterpret_cast<const uint2*>(block + lane * 8);
+}
+template <>
+__device__ __forceinline__ void read_frag<uint4>(const uint8_t* block, int lane, uint4& out) {
+    out = *reinterpret_cast<const uint4*>(block + lane * 16);
+}
+template <>
+__device__ __forceinline__ void read_frag<F6Frag>(const uint8_t* block, int lane, F6Frag& out) {
+    out.p0 = *reinterpret_cast<const uint4*>(block + lane * 16);
+    out.p1 = *reinterpret_cast<const uint2*>(block + 1024 + lane * 8);
+}
+
+template <int FMT, int NS>
 __device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, int wn, int wm,
-                                           int lane, RawFrags<ABITS>& fr) {
-    using C = Cfg<ABITS, NS>;
+                                           int lane, RawFrags<FMT>& fr) {
+    using C = Cfg<FMT, NS>;
     const uint8_t* wst = stage + C::kActBytes;
 #pragma unroll
     for (int f = 0; f < FW; ++f)
-        fr.w[f] = *reinterpret_cast<const uint2*>(wst + (wn * FW + f) * C::kWPerNb +
-                                                  kk * C::kWBlock + lane * 8);
+        read_frag(wst + (wn * FW + f) * C::kWPerNb + kk * C::kWBlock, lane, fr.w[f]);
 #pragma unroll
-    for (int g = 0; g < FA; ++g) {
-        const uint8_t* ap = stage + (wm * FA + g) * C::kActPerMb + kk * C::kActBlock;
-        if constexpr (ABITS == 8)
-            fr.a[g] = *reinterpret_cast<const uint4*>(ap + lane * 16);
-        else
-            fr.a[g] = *reinterpret_cast<const uint2*>(ap + lane * 8);
+    for (int g = 0; g < FA; ++g)
+        read_frag(stage + (wm * FA + g) * C::kActPerMb + kk * C::kActBlock, lane, fr.a[g]);
+}
+
+__device__ __forceinline__ v8i f6_operand(const F6Frag& f) {
+    return v8i{(int)f.p0.x, (int)f.p0.y, (int)f.p0.z, (int)f.p0.w, (int)f.p1.x, (int)f.p1.y,
+               0, 0};
+}
+
+// One k-substep: widen 4-bit fragments where needed and issue the FW x FA
+// MFMAs of the wave tile.
+template <int FMT>
+__device__ __forceinline__ void mma_substep(const RawFrags<FMT>& fr,
+                                            typename Fmt<FMT>::Acc (&acc)[FW][FA]) {
+    if constexpr (FMT == kFmtF6) {
+        v8i wf[FW], af[FA];
+#pragma unroll
+        for (int f = 0; f < FW; ++f) wf[f] = f6_operand(fr.w[f]);
+#pragma unroll
+        for (int g = 0; g < FA; ++g) af[g] = f6_operand(fr.a[g]);
+        // formats: 2 = FP6 E2M3 for both operands; scales 127 = 2^0 (E8M0)
+#pragma unroll
+        for (int f = 0; f < FW; ++f)
+#pragma unroll
+            for (int g = 0; g < FA; ++g)
+                acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    wf[f], af[g], acc[f][g], 2, 2, 0, 127, 0, 127);
+    } else {
+        v4i wf[FW], af[FA];
+#pragma unroll
+        for (int f = 0; f < FW; ++f) wf[f] = widen_nibbles(fr.w[f].x, fr.w[f].y);
+#pragma unroll
+        for (int g = 0; g < FA; ++g) {
+            if constexpr (FMT == kFmtA8)
+                af[g] = v4i{(int)fr.a[g].x, (int)fr.a[g].y, (int)fr.a[g].z, (int)fr.a[g].w};
+            else
+                af[g] = widen_nibbles(fr.a[g].x, fr.a[g].y);
+        }
+#pragma unroll
+        for (int f = 0; f < FW; ++f)
+#pragma unroll
+            for (int g = 0; g < FA; ++g)
+                acc[f][g] =
+                    __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[f], af[g], acc[f][g], 0, 0, 0);
     }
 }
 
-// Scheduling groups (LLVM AMDGPU sched_group_barrier masks).
-constexpr int kSchedVALU = 0x002;
-constexpr int kSchedMFMA = 0x008;
-constexpr int kSchedDSRead = 0x100;
-
-// One 32-wide k-substep: widen this substep's 4-bit fragments and issue its
-// FW x FA MFMAs.  The LDS reads of the next substep (already issued by the
-// caller, in program order before this call) and the widening ops are
-// interleaved with the MFMAs, so the wave keeps issuing independent work
-// while the matrix pipe is busy instead of stalling on a cluster of MFMAs.
-template <int ABITS>
-__device__ __forceinline__ void mma_substep(const RawFrags<ABITS>& fr, v16i (&acc)[FW][FA]) {
-    v4i wf[FW], af[FA];
-#pragma unroll
-    for (int f = 0; f < FW; ++f) wf[f] = widen_nibbles(fr.w[f].x, fr.w[f].y);
-#pragma unroll
-    for (int g = 0; g < FA; ++g) {
-        if constexpr (ABITS == 8)
-            af[g] = v4i{(int)fr.a[g].x, (int)fr.a[g].y, (int)fr.a[g].z, (int)fr.a[g].w};
-        else
-            af[g] = widen_nibbles(fr.a[g].x, fr.a[g].y);
-    }
-#pragma unroll
-    for (int f = 0; f < FW; ++f)
-#pragma unroll
-        for (int g = 0; g < FA; ++g)
-            acc[f][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[f], af[g], acc[f][g], 0, 0, 0);
-    // Interleave: each MFMA is followed by a few VALU ops and one LDS read.
-    constexpr int kValu = ABITS == 8 ? 6 * FW : 6 * (FW + FA);
-    constexpr int kMfma = FW * FA;
-    constexpr int kValuPer = (kValu + kMfma - 1) / kMfma;
-#pragma unroll
-    for (int i = 0; i < kMfma; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSchedVALU, kValuPer, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDSRead, 1, 0);
-    }
+// Exact integer value of an accumulator element (the int8 path carries 16x
+// (W4A8) or 256x (W4A4) the true sum, see widen_nibbles).
+template <int FMT>
+__device__ __forceinline__ int acc_value(const typename Fmt<FMT>::Acc& a, int r) {
+    if constexpr (FMT == kFmtF6) return (int)a[r];
+    else if constexpr (FMT == kFmtA8) return a[r] >> 4;
+    else return a[r] >> 8;
 }
 
-template <int ABITS, int NS, bool ACC_OUT>
+template <int FMT, int NS, bool ACC_OUT>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
     const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
     int32_t* __restrict__ acc_out, int tiles_m, int tiles_n) {
-    using C = Cfg<ABITS, NS>;
+    using C = Cfg<FMT, NS>;
+    using F = Fmt<FMT>;
     constexpr int L = C::kLoads;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
@@ -240,7 +316,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
 
     int tile_m, tile_n;
     tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tile_m, tile_n);
-    const int kblocks = K >> 5;
+    const int kblocks = K / F::kKSub;                       // code blocks along k
     const int mblocks = (M + 31) >> 5;
     const int nblocks = N >> 5;
     const int ksteps = K / BK;
@@ -324,7 +400,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             load_lds16(w_src[i] + w_off, voff, base + w_dst[i]);
     };
 
-    v16i acc[FW][FA];
+    typename F::Acc acc[FW][FA];
 #pragma unroll
     for (int f = 0; f < FW; ++f)
 #pragma unroll
@@ -342,19 +418,20 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     // barrier that admits stage kt+1 sits after the reads of stage kt's last
     // substep and before its MFMAs, so the MFMA pipe has work queued while
     // the workgroup synchronizes and the next stage's first fragments load.
-    // Fragments are read two k-substeps ahead of the MFMAs that use them
-    // (global substep j = kt * P + kk uses register set fr[j % 4]).  The
+    // Fragments are read D k-substeps ahead of the MFMAs that use them
+    // (global substep j = kt * P + kk uses register set fr[j % NSETS]).  The
     // barrier that admits stage kt+1 sits right before the first read of
     // that stage, after every read of stage kt, so the MFMA pipe still has
     // queued substeps while the workgroup synchronizes.
-    constexpr int P = BK / 32;                       // substeps per stage
-    constexpr int D = 2;                             // read-ahead distance
-    constexpr int U = 4 / P;                         // stages per unrolled iteration
-    static_assert(P * U == 4 && D <= P * U, "substep bookkeeping");
-    RawFrags<ABITS> fr[4];
+    constexpr int P = BK / F::kKSub;                 // substeps per stage
+    constexpr int D = F::kReadAhead;                 // read-ahead distance
+    constexpr int NSETS = 2 * D;                     // register sets in rotation
+    constexpr int U = NSETS / P;                     // stages per unrolled iteration
+    static_assert(U >= 1 && P * U == NSETS && D <= P, "substep bookkeeping");
+    RawFrags<FMT> fr[NSETS];
 #pragma unroll
     for (int j = 0; j < D; ++j)
-        read_frags<ABITS, NS>(lds + (j / P) * C::kStageBytes, j % P, wn, wm, lane, fr[j]);
+        read_frags<FMT, NS>(lds + (j / P) * C::kStageBytes, j % P, wn, wm, lane, fr[j]);
     for (int kt0 = 0; kt0 < ksteps; kt0 += U) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -362,7 +439,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             if (kt < ksteps) {
 #pragma unroll
                 for (int kk = 0; kk < P; ++kk) {
-                    const int j = u * P + kk;                // substep index mod 4
+                    const int j = u * P + kk;                // substep index mod NSETS
                     const int ahead = kk + D;                // substep to read, relative to stage kt
                     const int rk = ahead % P;
                     const int rst = kt + ahead / P;          // its stage
@@ -372,10 +449,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                             wait_stages_and_barrier<L>(min(NS - 2, ksteps - 2 - kt));
                             if (kt + NS < ksteps) issue_stage(kt + NS);
                         }
-                        read_frags<ABITS, NS>(lds + (rst % NS) * C::kStageBytes, rk, wn, wm,
-                                              lane, fr[(j + D) % 4]);
+                        read_frags<FMT, NS>(lds + (rst % NS) * C::kStageBytes, rk, wn, wm, lane,
+                                            fr[(j + D) % NSETS]);
                     }
-                    mma_substep<ABITS>(fr[j], acc);
+                    mma_substep<FMT>(fr[j], acc);
                 }
             }
         }
@@ -389,7 +466,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     //    from the LDS tables.
     // 2. each wave stores its own rows: 8 lanes per 128-byte row, so every
     //    store instruction writes whole cache lines.
-    constexpr int kShift = ABITS == 8 ? 4 : 8;
     constexpr int kWaveRowBytes = FW * 32 * 2;                 // 128
     constexpr int kWaveRows = FA * 32;                         // 128
     __syncthreads();                                   // ring no longer read
@@ -410,10 +486,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                 const float rs = row_rs[g];
                 const float4 a = *reinterpret_cast<const float4*>(tab + 256 * (1 + s) + ti);
                 const float4 b = *reinterpret_cast<const float4*>(tab + 256 * (1 + S + s) + ti);
-                const int v0 = acc[f][g][4 * q + 0] >> kShift;
-                const int v1 = acc[f][g][4 * q + 1] >> kShift;
-                const int v2 = acc[f][g][4 * q + 2] >> kShift;
-                const int v3 = acc[f][g][4 * q + 3] >> kShift;
+                const int v0 = acc_value<FMT>(acc[f][g], 4 * q + 0);
+                const int v1 = acc_value<FMT>(acc[f][g], 4 * q + 1);
+                const int v2 = acc_value<FMT>(acc[f][g], 4 * q + 2);
+                const int v3 = acc_value<FMT>(acc[f][g], 4 * q + 3);
                 const float y0 = __builtin_fmaf(a.x, (float)v0 * (rs * ws.x), b.x);
                 const float y1 = __builtin_fmaf(a.y, (float)v1 * (rs * ws.y), b.y);
                 const float y2 = __builtin_fmaf(a.z, (float)v2 * (rs * ws.z), b.z);
@@ -453,62 +529,61 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     }
 }
 
-template <int ABITS, int NS, bool ACC_OUT>
+template <int FMT, int NS, bool ACC_OUT>
 hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                           const uint8_t* Wq, const float* w_scale, const float* comp_a,
                           const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                           int32_t* acc_out, hipStream_t stream) {
-    using C = Cfg<ABITS, NS>;
+    using C = Cfg<FMT, NS>;
     static_assert(C::lds_bytes(1) <= kLdsLimit, "LDS budget");
     static_assert(C::lds_bytes(RUDDER_MAX_STREAMS) <= 160 * 1024, "LDS budget");
     // the attribute admits the full CU; a call whose tables do not fit the
     // per-workgroup share simply runs fewer workgroups per CU
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)w4_gemm_kernel<ABITS, NS, ACC_OUT>,
+        (const void*)w4_gemm_kernel<FMT, NS, ACC_OUT>,
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((w4_gemm_kernel<ABITS, NS, ACC_OUT>), dim3((unsigned)(tiles_m * tiles_n)),
+    hipLaunchKernelGGL((w4_gemm_kernel<FMT, NS, ACC_OUT>), dim3((unsigned)(tiles_m * tiles_n)),
                        dim3(kThreads), C::lds_bytes(S), stream, xq, row_scale, sid, Wq, w_scale,
                        comp_a, comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n);
     return hipGetLastError();
 }
 
-template <int ABITS, bool ACC_OUT>
-hipError_t launch_bits(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
-                       const uint8_t* Wq, const float* w_scale, const float* comp_a,
-                       const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
-                       int32_t* acc_out, hipStream_t stream) {
-    // deepest ring that fits together with this call's tables
-    constexpr int NS_MAX = ABITS == 8 ? 2 : 3;
-    if (Cfg<ABITS, NS_MAX>::lds_bytes(S) <= kLdsLimit)
-        return launch_variant<ABITS, NS_MAX, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                      comp_b, M, N, K, S, Y, acc_out, stream);
-    constexpr int NS_MIN = NS_MAX > 2 ? NS_MAX - 1 : 2;
-    return launch_variant<ABITS, NS_MIN, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                      comp_b, M, N, K, S, Y, acc_out, stream);
+template <int FMT, bool ACC_OUT>
+hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+                      const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                      const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
+                      int32_t* acc_out, hipStream_t stream) {
+    // deepest ring that fits the per-workgroup LDS share with this call's tables
+    constexpr int NS_MAX = FMT == kFmtA4 ? 3 : 2;
+    if constexpr (NS_MAX > 2) {
+        if (Cfg<FMT, NS_MAX>::lds_bytes(S) > kLdsLimit)
+            return launch_variant<FMT, NS_MAX - 1, ACC_OUT>(xq, row_scale, sid, Wq, w_scale,
+                                                            comp_a, comp_b, M, N, K, S, Y,
+                                                            acc_out, stream);
+    }
+    return launch_variant<FMT, NS_MAX, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
+                                                M, N, K, S, Y, acc_out, stream);
 }
 
 }  // namespace
 
 hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* sid,
                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
-                         const float* comp_b, int M, int N, int K, int S, int abits, uint16_t* Y,
-                         int32_t* acc_out, hipStream_t stream) {
+                         const float* comp_b, int M, int N, int K, int S, int abits, int codes,
+                         uint16_t* Y, int32_t* acc_out, hipStream_t stream) {
     const uint8_t* xq = static_cast<const uint8_t*>(Xq);
-    if (abits == 8) {
-        if (acc_out)
-            return launch_bits<8, true>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
-                                        S, Y, acc_out, stream);
-        return launch_bits<8, false>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S,
-                                     Y, acc_out, stream);
-    }
-    if (acc_out)
-        return launch_bits<4, true>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S,
-                                    Y, acc_out, stream);
-    return launch_bits<4, false>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S, Y,
-                                 acc_out, stream);
+#define RUDDER_LAUNCH(FMT)                                                                   \
+    return acc_out ? launch_fmt<FMT, true>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, \
+                                           N, K, S, Y, acc_out, stream)                       \
+                   : launch_fmt<FMT, false>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,  \
+                                            M, N, K, S, Y, acc_out, stream)
+    if (codes == RUDDER_CODES_E2M3) RUDDER_LAUNCH(kFmtF6);
+    if (abits == 8) RUDDER_LAUNCH(kFmtA8);
+    RUDDER_LAUNCH(kFmtA4);
+#undef RUDDER_LAUNCH
 }
 
 }  // namespace rudder

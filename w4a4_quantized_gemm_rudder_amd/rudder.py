@@ -21,6 +21,9 @@ from typing import Optional, Tuple
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_lib", "librudder.so")
 
+CODES_INT = 0       # int4 split-nibble / int8 codes (int8 matrix cores)
+CODES_E2M3 = 1      # 4-bit codes held as FP6 E2M3 (W4A4; f8f6f4 matrix cores)
+
 RUDDER_OK = 0
 RUDDER_ERR_INVALID_ARG = 1
 RUDDER_ERR_UNSUPPORTED = 2
@@ -53,17 +56,17 @@ def load_library() -> ctypes.CDLL:
                           "or python w4a4_quantized_gemm_rudder_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-    lib.rudder_packed_weight_bytes.argtypes = [i, i]
+    lib.rudder_packed_weight_bytes.argtypes = [i, i, i]
     lib.rudder_packed_weight_bytes.restype = sz
-    lib.rudder_packed_act_bytes.argtypes = [i, i, i]
+    lib.rudder_packed_act_bytes.argtypes = [i, i, i, i]
     lib.rudder_packed_act_bytes.restype = sz
     lib.rudder_quant_act_workspace_bytes.argtypes = [i]
     lib.rudder_quant_act_workspace_bytes.restype = sz
-    lib.rudder_quantize_weights.argtypes = [vp, vp, i, i, vp, vp, vp, vp]
+    lib.rudder_quantize_weights.argtypes = [vp, vp, i, i, i, vp, vp, vp, vp]
     lib.rudder_quantize_weights.restype = i
-    lib.rudder_quant_act.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, vp, vp, vp]
+    lib.rudder_quant_act.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.rudder_quant_act.restype = i
-    lib.rudder_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
+    lib.rudder_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp]
     lib.rudder_linear.restype = i
     lib.rudder_status_string.argtypes = [i]
     lib.rudder_status_string.restype = ctypes.c_char_p
@@ -104,12 +107,12 @@ def _stream(stream) -> Optional[int]:
 # Size helpers
 # ---------------------------------------------------------------------------
 
-def packed_weight_bytes(K: int, N: int) -> int:
-    return int(load_library().rudder_packed_weight_bytes(K, N))
+def packed_weight_bytes(K: int, N: int, codes: int = CODES_INT) -> int:
+    return int(load_library().rudder_packed_weight_bytes(K, N, codes))
 
 
-def packed_act_bytes(M: int, K: int, abits: int) -> int:
-    return int(load_library().rudder_packed_act_bytes(M, K, abits))
+def packed_act_bytes(M: int, K: int, abits: int, codes: int = CODES_INT) -> int:
+    return int(load_library().rudder_packed_act_bytes(M, K, abits, codes))
 
 
 def quant_act_workspace_bytes(S: int) -> int:
@@ -122,67 +125,70 @@ def quant_act_workspace_bytes(S: int) -> int:
 # int16/uint16 bit patterns)
 # ---------------------------------------------------------------------------
 
-def rudder_quantize_weights(W, smooth, K: int, N: int, Wq, w_scale, inv_smooth,
+def rudder_quantize_weights(W, smooth, K: int, N: int, codes: int, Wq, w_scale, inv_smooth,
                             stream=None) -> None:
     _check(load_library().rudder_quantize_weights(
-        _ptr(W), _ptr(smooth), K, N, _ptr(Wq), _ptr(w_scale), _ptr(inv_smooth), _stream(stream)))
+        _ptr(W), _ptr(smooth), K, N, codes, _ptr(Wq), _ptr(w_scale), _ptr(inv_smooth),
+        _stream(stream)))
 
 
 def rudder_quant_act(X, stream_id, inv_smooth, act_scale, act_scale_out, workspace,
-                     M: int, K: int, S: int, abits: int, Xq, row_scale, stream=None) -> None:
+                     M: int, K: int, S: int, abits: int, codes: int, Xq, row_scale,
+                     stream=None) -> None:
     _check(load_library().rudder_quant_act(
         _ptr(X), _ptr(stream_id), _ptr(inv_smooth), _ptr(act_scale), _ptr(act_scale_out),
-        _ptr(workspace), M, K, S, abits, _ptr(Xq), _ptr(row_scale), _stream(stream)))
+        _ptr(workspace), M, K, S, abits, codes, _ptr(Xq), _ptr(row_scale), _stream(stream)))
 
 
 def rudder_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b,
-                  M: int, N: int, K: int, S: int, abits: int, Y, acc_out=None,
+                  M: int, N: int, K: int, S: int, abits: int, codes: int, Y, acc_out=None,
                   stream=None) -> None:
     _check(load_library().rudder_linear(
         _ptr(Xq), _ptr(row_scale), _ptr(stream_id), _ptr(Wq), _ptr(w_scale), _ptr(comp_a),
-        _ptr(comp_b), M, N, K, S, abits, _ptr(Y), _ptr(acc_out), _stream(stream)))
+        _ptr(comp_b), M, N, K, S, abits, codes, _ptr(Y), _ptr(acc_out), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------
 # Allocating conveniences (torch allocates; the library computes)
 # ---------------------------------------------------------------------------
 
-def quantize_weights(W, smooth, stream=None):
+def quantize_weights(W, smooth, codes: int = CODES_INT, stream=None):
     """W: bf16 [K, N] device tensor, smooth: fp32 [K].
-    Returns (Wq uint8 [N*K/2], w_scale fp32 [N], inv_smooth fp32 [K])."""
+    Returns (Wq uint8, w_scale fp32 [N], inv_smooth fp32 [K])."""
     import torch
     K, N = W.shape
     dev = W.device
-    Wq = torch.empty(packed_weight_bytes(K, N), dtype=torch.uint8, device=dev)
+    Wq = torch.empty(packed_weight_bytes(K, N, codes), dtype=torch.uint8, device=dev)
     w_scale = torch.empty(N, dtype=torch.float32, device=dev)
     inv_smooth = torch.empty(K, dtype=torch.float32, device=dev)
-    rudder_quantize_weights(W, smooth, K, N, Wq, w_scale, inv_smooth, stream)
+    rudder_quantize_weights(W, smooth, K, N, codes, Wq, w_scale, inv_smooth, stream)
     return Wq, w_scale, inv_smooth
 
 
-def quant_act(X, stream_id, inv_smooth, act_scale, S: int, abits: int, stream=None,
-              act_scale_out=None, workspace=None):
+def quant_act(X, stream_id, inv_smooth, act_scale, S: int, abits: int, codes: int = CODES_INT,
+              stream=None, act_scale_out=None, workspace=None):
     """X: bf16 [M, K].  act_scale: fp32 [S] device tensor, or None for dynamic
     (absmax) step sizes.  Returns (Xq uint8, row_scale fp32 [M])."""
     import torch
     M, K = X.shape
     dev = X.device
-    Xq = torch.empty(max(packed_act_bytes(M, K, abits), 1), dtype=torch.uint8, device=dev)
+    Xq = torch.empty(max(packed_act_bytes(M, K, abits, codes), 1), dtype=torch.uint8,
+                     device=dev)
     row_scale = torch.empty(max(M, 1), dtype=torch.float32, device=dev)
     if act_scale is None and workspace is None:
         workspace = torch.empty(quant_act_workspace_bytes(S), dtype=torch.uint8, device=dev)
     rudder_quant_act(X, stream_id, inv_smooth, act_scale, act_scale_out, workspace, M, K, S,
-                     abits, Xq, row_scale, stream)
+                     abits, codes, Xq, row_scale, stream)
     return Xq, row_scale
 
 
 def linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b, M: int, N: int, K: int,
-           S: int, abits: int, stream=None, acc_out: bool = False):
+           S: int, abits: int, codes: int = CODES_INT, stream=None, acc_out: bool = False):
     """Returns Y bf16 [M, N] (and int32 accumulators [M, N] if acc_out)."""
     import torch
     dev = Wq.device
     Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     acc = torch.empty((M, N), dtype=torch.int32, device=dev) if acc_out else None
     rudder_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b, M, N, K, S, abits,
-                  Y, acc, stream)
+                  codes, Y, acc, stream)
     return (Y, acc) if acc_out else Y

@@ -6,7 +6,8 @@ proprio, 128 action): QKV 2048->6144 and O 2048->2048 at W4A8, MLP up
 2048->8192 and down 8192->2048 at W4A4.  Each linear is one
 rudder_quant_act (fused smoothing + per-(stream, step) quantization) and one
 rudder_linear (int8-MFMA GEMM + fused dequant/compensation epilogue), i.e. 8
-launches per step; the step index cycles through the 16-step denoise loop,
+launches per step (the W4A4 linears hold their 4-bit codes as FP6 E2M3 by
+default, see --w4a4-codes); the step index cycles through the 16-step denoise loop,
 selecting that step's activation step sizes and compensation vectors
 (SteerQuant §4.3 layer-step table, §4.4 Rudder).  Weights are prepared once
 before timing (offline preparation, SteerQuant Fig. 2).  All inputs are
@@ -21,10 +22,12 @@ CPU oracle on a bounded sample of the same step.
 
 --workload picks another workload (each printed as one JSON line of the
 same form, steps cycling through its step-indexed scale sets).
---w4a4-codes picks the code container of the W4A4 linears: "int" (int4
-codes widened to int8 for the int8 matrix cores) or "e2m3" (the same 4-bit
-codes held as FP6 E2M3 for the f8f6f4 matrix cores, fp32 accumulation, exact
-for integer codes).  Outputs are identical either way.
+--w4a4-codes picks the code container of the W4A4 linears: "e2m3" (default:
+the 4-bit codes held as FP6 E2M3 for the f8f6f4 matrix cores, fp32
+accumulation, exact for integer codes) or "int" (int4 codes widened to int8
+for the int8 matrix cores).  Outputs are identical either way.
+Comparators (context only): torch.matmul in bf16 and torch._int_mm (hipBLASLt
+int8 GEMM, no quantization or epilogue) on the same shapes.
 """
 from __future__ import annotations
 
@@ -67,10 +70,11 @@ def parse_args():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--seed", type=int, default=0)
-    p.add_argument("--w4a4-codes", choices=["int", "e2m3"], default="int",
-                   help="code container of the W4A4 linears")
+    p.add_argument("--w4a4-codes", choices=["int", "e2m3"], default="e2m3",
+                   help="code container of the W4A4 linears (identical outputs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-bf16", action="store_true", help="skip the bf16 matmul comparator")
+    p.add_argument("--no-bf16", action="store_true",
+                   help="skip the library comparators (bf16 matmul, int8 GEMM)")
     p.add_argument("--cpu-rows", type=int, default=8384,
                    help="rows per linear in the CPU-oracle sample")
     p.add_argument("--cpu-steps", type=int, default=6,
@@ -228,6 +232,32 @@ def bf16_comparator(wl, layers, torch, reps: int = 10):
     return tot * 1e3      # µs per step
 
 
+def int8_library_comparator(wl, layers, torch, reps: int = 10):
+    """hipBLASLt int8 x int8 -> int32 GEMM (torch._int_mm) on the same
+    [M,K] x [K,N] shapes: a plain library integer GEMM with no quantization,
+    no scales and no epilogue, for context.  Returns µs per step or None."""
+    tot = 0.0
+    for Ly in layers:
+        a = torch.randint(-127, 128, (wl.M, Ly["K"]), dtype=torch.int8, device="cuda")
+        b = torch.randint(-7, 8, (Ly["N"], Ly["K"]), dtype=torch.int8, device="cuda").t()
+        try:
+            for _ in range(3):
+                torch._int_mm(a, b)
+        except Exception:
+            return None
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch._int_mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        tot += e0.elapsed_time(e1) / reps
+        del a, b
+    return tot * 1e3
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -347,6 +377,9 @@ def main():
         bf16_us = bf16_comparator(wl, layers, torch)
         out["bf16_matmul_us_per_step"] = round(bf16_us, 1)
         out["speedup_vs_bf16_matmul"] = round(bf16_us / (ms_per_step * 1e3), 3)
+        i8_us = int8_library_comparator(wl, layers, torch)
+        if i8_us is not None:
+            out["int8_library_gemm_us_per_step"] = round(i8_us, 1)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.cpu_steps, args.seed)
     print(json.dumps(out), flush=True)

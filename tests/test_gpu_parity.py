@@ -72,12 +72,7 @@ RAGGED_E2M3 = [
 ]
 
 
-@pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes",
-                         [r + (CODES_INT,) for r in RAGGED] +
-                         [r + (CODES_E2M3,) for r in RAGGED_E2M3])
-def test_ragged_shapes(M, K, N, S, abits, dynamic, seed, codes):
-    log(f"case ragged M={M} K={K} N={N} S={S} abits={abits} dynamic={dynamic} seed={seed} "
-        f"codes={codes}")
+def _random_layer_case(M, K, N, S, abits, dynamic, seed, codes):
     rng = np.random.default_rng(1000 + seed)
     x = rng.standard_normal((M, K))
     x[:, rng.integers(0, K, 3)] *= 25.0
@@ -97,8 +92,39 @@ def test_ragged_shapes(M, K, N, S, abits, dynamic, seed, codes):
         qa = 127 if abits == 8 else 7
         u = np.abs(x / s[None, :]).max()
         delta = (rng.uniform(0.5, 1.0, S) * u / qa).astype(np.float32)
-    st = run.run_step(delta, a, b, label=f"ragged{seed}")
-    log(f"  {st}")
+    return run.run_step(delta, a, b, label=f"case{seed}")
+
+
+@pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes",
+                         [r + (CODES_INT,) for r in RAGGED] +
+                         [r + (CODES_E2M3,) for r in RAGGED_E2M3])
+def test_ragged_shapes(M, K, N, S, abits, dynamic, seed, codes):
+    log(f"case ragged M={M} K={K} N={N} S={S} abits={abits} dynamic={dynamic} seed={seed} "
+        f"codes={codes}")
+    log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
+
+
+# Few-row calls (the weight-streaming kernel): action/proprio-sized M against
+# full-width weights, both sides of the row-count switch, every container.
+SMALL_M = [
+    # M, K, N, S, abits, dynamic, seed, codes
+    (96, 2048, 6144, 3, 8, True, 20, CODES_INT),
+    (64, 2048, 2048, 3, 8, False, 21, CODES_INT),
+    (65, 2048, 2048, 2, 8, False, 22, CODES_INT),
+    (128, 4096, 1024, 3, 4, False, 23, CODES_INT),
+    (129, 1024, 512, 3, 4, True, 24, CODES_INT),
+    (32, 8192, 2048, 3, 4, False, 25, CODES_E2M3),
+    (100, 4096, 12288, 3, 4, True, 26, CODES_E2M3),
+    (128, 128, 96, 5, 4, False, 27, CODES_E2M3),
+    (2, 256, 64, 2, 8, True, 28, CODES_INT),
+]
+
+
+@pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes", SMALL_M)
+def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
+    log(f"case small-M M={M} K={K} N={N} S={S} abits={abits} dynamic={dynamic} seed={seed} "
+        f"codes={codes}")
+    log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
 
 
 @pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3)])

@@ -50,13 +50,9 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int BM = 128;          // tokens per block tile
 constexpr int BN = 256;          // output channels per block tile
 constexpr int BK = 128;          // k per pipeline stage (4 MFMA k-steps)
-constexpr int kWavesN = 4;       // waves along the channel dimension
-constexpr int kWavesM = 1;       // waves along the token dimension
 constexpr int kBlocksPerCU = 2;  // two independent workgroups share each CU
-constexpr int kWaves = kWavesN * kWavesM;
+constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int FW = BN / kWavesN / 32;   // 32-channel fragments per wave (2)
-constexpr int FA = BM / kWavesM / 32;   // 32-token fragments per wave (4)
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;       // m-tiles per tile group (L2 reuse of weight panels)
 
@@ -71,6 +67,11 @@ struct F6Frag {
     uint2 p1;
 };
 
+// Per-format traits.  The wave grid (kWavesN x kWavesM) splits the 128 x 256
+// block tile; each wave owns FW 32-channel and FA 32-token fragments, so
+// every k-substep it reads FW weight and FA activation fragments from LDS and
+// issues FW * FA MFMAs.  (With int8 activations a 2 x 2 grid reads 20% fewer
+// LDS bytes per MFMA than 1 x 4, and measured no faster.)
 template <int FMT>
 struct Fmt;
 template <>
@@ -79,6 +80,7 @@ struct Fmt<kFmtA8> {
     static constexpr int kABlock = 1024;   // bytes per 32-row x kKSub code block
     static constexpr int kWBlock = 512;
     static constexpr int kReadAhead = 2;   // substeps of fragment read-ahead
+    static constexpr int kWavesN = 4;      // waves along the channel dimension
     typedef uint2 WFrag;
     typedef uint4 AFrag;
     typedef v16i Acc;
@@ -89,6 +91,7 @@ struct Fmt<kFmtA4> {
     static constexpr int kABlock = 512;
     static constexpr int kWBlock = 512;
     static constexpr int kReadAhead = 2;
+    static constexpr int kWavesN = 4;
     typedef uint2 WFrag;
     typedef uint2 AFrag;
     typedef v16i Acc;
@@ -99,9 +102,19 @@ struct Fmt<kFmtF6> {
     static constexpr int kABlock = 1536;
     static constexpr int kWBlock = 1536;
     static constexpr int kReadAhead = 1;
+    static constexpr int kWavesN = 4;
     typedef F6Frag WFrag;
     typedef F6Frag AFrag;
     typedef v16f Acc;
+};
+
+template <int FMT>
+struct Waves {
+    static constexpr int kN = Fmt<FMT>::kWavesN;          // waves along channels
+    static constexpr int kM = kWaves / kN;                // waves along tokens
+    static constexpr int FW = BN / kN / 32;               // 32-channel fragments per wave
+    static constexpr int FA = BM / kM / 32;               // 32-token fragments per wave
+    static_assert(kN * kM == kWaves && FW * kN * 32 == BN && FA * kM * 32 == BM, "wave grid");
 };
 
 template <int FMT, int NS>
@@ -210,8 +223,8 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblk, int tiles_m, in
 // Raw (still packed) fragment words of one k-substep.
 template <int FMT>
 struct RawFrags {
-    typename Fmt<FMT>::WFrag w[FW];                 // channel blocks
-    typename Fmt<FMT>::AFrag a[FA];                 // token blocks
+    typename Fmt<FMT>::WFrag w[Waves<FMT>::FW];     // channel blocks
+    typename Fmt<FMT>::AFrag a[Waves<FMT>::FA];     // token blocks
 };
 
 template <typename T>
@@ -234,6 +247,7 @@ template <int FMT, int NS>
 __device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, int wn, int wm,
                                            int lane, RawFrags<FMT>& fr) {
     using C = Cfg<FMT, NS>;
+    constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
     const uint8_t* wst = stage + C::kActBytes;
 #pragma unroll
     for (int f = 0; f < FW; ++f)
@@ -243,6 +257,8 @@ __device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, int wn,
         read_frag(stage + (wm * FA + g) * C::kActPerMb + kk * C::kActBlock, lane, fr.a[g]);
 }
 
+// The 8-dword MFMA operand of an E2M3 fragment (the instruction reads the
+// first 6 dwords for FP6 operands).
 __device__ __forceinline__ v8i f6_operand(const F6Frag& f) {
     return v8i{(int)f.p0.x, (int)f.p0.y, (int)f.p0.z, (int)f.p0.w, (int)f.p1.x, (int)f.p1.y,
                0, 0};
@@ -251,8 +267,9 @@ __device__ __forceinline__ v8i f6_operand(const F6Frag& f) {
 // One k-substep: widen 4-bit fragments where needed and issue the FW x FA
 // MFMAs of the wave tile.
 template <int FMT>
-__device__ __forceinline__ void mma_substep(const RawFrags<FMT>& fr,
-                                            typename Fmt<FMT>::Acc (&acc)[FW][FA]) {
+__device__ __forceinline__ void mma_substep(
+    const RawFrags<FMT>& fr, typename Fmt<FMT>::Acc (&acc)[Waves<FMT>::FW][Waves<FMT>::FA]) {
+    constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
     if constexpr (FMT == kFmtF6) {
         v8i wf[FW], af[FA];
 #pragma unroll
@@ -305,6 +322,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     using C = Cfg<FMT, NS>;
     using F = Fmt<FMT>;
     constexpr int L = C::kLoads;
+    constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
+    constexpr int kWavesN = Waves<FMT>::kN;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -322,16 +341,22 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const int ksteps = K / BK;
     const int n_tile0 = min(tile_n * BN, N - 32);            // first channel of the tile (clamped)
 
-    // Row data of this lane's two token rows, fetched before the main loop
-    // (plain loads; the compiler waits for them only in the epilogue).
+    // Stream id and row scale of this lane's FA token rows (plain loads; the
+    // compiler waits for them only in the epilogue).  The int formats fetch
+    // them before the main loop; the E2M3 loop has no registers to hold them
+    // across it, so it fetches them after the loop.
+    constexpr bool kLateRowData = FMT == kFmtF6;
     int row_stream[FA];
     float row_rs[FA];
+    auto fetch_row_data = [&]() {
 #pragma unroll
-    for (int g = 0; g < FA; ++g) {
-        const int mc = min(tile_m * BM + wm * (FA * 32) + g * 32 + (lane & 31), M - 1);
-        row_stream[g] = sid[mc] & (RUDDER_MAX_STREAMS - 1);
-        row_rs[g] = row_scale[mc];
-    }
+        for (int g = 0; g < FA; ++g) {
+            const int mc = min(tile_m * BM + wm * (FA * 32) + g * 32 + (lane & 31), M - 1);
+            row_stream[g] = min(sid[mc] & (RUDDER_MAX_STREAMS - 1), S - 1);
+            row_rs[g] = row_scale[mc];
+        }
+    };
+    if constexpr (!kLateRowData) fetch_row_data();
 
     // ---- epilogue tables -> LDS (one KiB per table row, one wave each) ----
     // row 0: w_scale, rows 1..S: comp_a[s], rows S+1..2S: comp_b[s], each for
@@ -426,8 +451,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     constexpr int P = BK / F::kKSub;                 // substeps per stage
     constexpr int D = F::kReadAhead;                 // read-ahead distance
     constexpr int NSETS = 2 * D;                     // register sets in rotation
-    constexpr int U = NSETS / P;                     // stages per unrolled iteration
-    static_assert(U >= 1 && P * U == NSETS && D <= P, "substep bookkeeping");
+    constexpr int U = NSETS > P ? NSETS / P : 1;     // stages per unrolled iteration
+    static_assert((P * U) % NSETS == 0 && D <= P, "substep bookkeeping");
     RawFrags<FMT> fr[NSETS];
 #pragma unroll
     for (int j = 0; j < D; ++j)
@@ -439,7 +464,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             if (kt < ksteps) {
 #pragma unroll
                 for (int kk = 0; kk < P; ++kk) {
-                    const int j = u * P + kk;                // substep index mod NSETS
+                    const int j = (u * P + kk) % NSETS;      // substep index mod NSETS
                     const int ahead = kk + D;                // substep to read, relative to stage kt
                     const int rk = ahead % P;
                     const int rst = kt + ahead / P;          // its stage
@@ -462,12 +487,16 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     // 1. registers: t = float(acc) * (row_scale * w_scale); y = fma(a, t, b);
     //    bf16 (hardware round-to-nearest-even pack) into this wave's LDS
     //    staging area [FA*32 token rows][FW*32 channels]; 16-byte chunk c of
-    //    row r sits at chunk c ^ ((r >> 1) & 7).  Per-channel values come
-    //    from the LDS tables.
-    // 2. each wave stores its own rows: 8 lanes per 128-byte row, so every
-    //    store instruction writes whole cache lines.
-    constexpr int kWaveRowBytes = FW * 32 * 2;                 // 128
-    constexpr int kWaveRows = FA * 32;                         // 128
+    //    row r sits at chunk c ^ swz(r), which spreads the 32 rows one
+    //    instruction writes over the LDS banks.  Per-channel values come from
+    //    the LDS tables.
+    // 2. each wave stores its own rows: FW*4 lanes per row (128 or 256
+    //    bytes), so every store instruction writes whole cache lines.
+    constexpr int kWaveRowBytes = FW * 32 * 2;                 // 128 or 256
+    constexpr int kWaveRows = FA * 32;                         // 128 or 64
+    constexpr int kRowChunks = kWaveRowBytes / 16;             // 8 or 16
+    if constexpr (kLateRowData) fetch_row_data();
+    auto swz = [](int r) { return kRowChunks == 8 ? ((r >> 1) & 7) : (r & 15); };
     __syncthreads();                                   // ring no longer read
     const float* tab = reinterpret_cast<const float*>(lds + C::kTableOffset);
     const int tab_shift = tile_n * BN - (N >= BN ? min(n_tile0, N - BN) : 0);
@@ -498,9 +527,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                 packed.x = pack_bf16x2_rne(y0, y1);
                 packed.y = pack_bf16x2_rne(y2, y3);
                 const int r = g * 32 + (lane & 31);
-                *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes +
-                                          ((chunk ^ ((r >> 1) & 7)) * 16) + (lane >> 5) * 8) =
-                    packed;
+                *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes + ((chunk ^ swz(r)) * 16) +
+                                          (lane >> 5) * 8) = packed;
                 if constexpr (ACC_OUT) {
                     const int m = tile_m * BM + wm * kWaveRows + r;
                     const int n = tile_n * BN + nl;
@@ -516,17 +544,262 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     }
     // 2. whole-line stores of this wave's rows (its own LDS writes are
     //    ordered before these reads)
-    const int c = lane & 7;
+    constexpr int kRowsPerStore = 64 / kRowChunks;
+    const int c = lane & (kRowChunks - 1);
     const int m0 = tile_m * BM + wm * kWaveRows;
     const int n = tile_n * BN + wn * (FW * 32) + c * 8;
 #pragma unroll 4
-    for (int i = 0; i < kWaveRows / 8; ++i) {
-        const int r = i * 8 + (lane >> 3);
-        const uint4 v = *reinterpret_cast<const uint4*>(wstage + r * kWaveRowBytes +
-                                                        ((c ^ ((r >> 1) & 7)) * 16));
+    for (int i = 0; i < kWaveRows / kRowsPerStore; ++i) {
+        const int r = i * kRowsPerStore + lane / kRowChunks;
+        const uint4 v =
+            *reinterpret_cast<const uint4*>(wstage + r * kWaveRowBytes + ((c ^ swz(r)) * 16));
         if (m0 + r < M && n < N)
             *reinterpret_cast<uint4*>(Y + (size_t)(m0 + r) * N + n) = v;
     }
+}
+
+// ---------------------------------------------------------------------------
+// Small-M path (few token rows: action / proprio-only calls).  The weights
+// dominate the traffic, so the kernel is organised around streaming them
+// at HBM rate: one workgroup per 32-channel block of the output and group of
+// up to 32 * FA token rows (all rows in registers), the k range split
+// across the workgroup's waves.  Fragments come straight from global memory (the tiled
+// code layouts are lane-ordered, so every fragment is one contiguous load);
+// there is no LDS ring and no barrier in the k loop.  Each wave's partial
+// accumulators are summed into an LDS tile with LDS atomic adds: int32
+// addition, and fp32 addition of integers below 2^24, give the same result in
+// any order, so the sum is the exact dot product.  The epilogue applies the
+// same arithmetic as the tiled kernel and stores 16-byte row segments.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyWaves = 8;
+constexpr int kSkinnyMaxM = 256;                 // rows handled by the small-M kernel
+constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
+constexpr int kSkinnyPitch = 33;                 // LDS row pitch (words) of the sum tile
+
+// Operand registers of one k-substep: the weight fragment and up to FA
+// activation fragments, already in MFMA operand form (E2M3 fragments are
+// loaded straight into 8-dword operands whose top two dwords stay zero).
+template <int FMT, int FA>
+struct SkinnyOps {
+    typedef typename std::conditional<FMT == kFmtF6, v8i, uint2>::type WOp;
+    typedef typename std::conditional<FMT == kFmtF6, v8i,
+            typename std::conditional<FMT == kFmtA8, uint4, uint2>::type>::type AOp;
+    WOp w;
+    AOp a[FA];
+};
+
+__device__ __forceinline__ v8i load_f6_operand(const uint8_t* block, int lane) {
+    const uint4 p0 = *reinterpret_cast<const uint4*>(block + lane * 16);
+    const uint2 p1 = *reinterpret_cast<const uint2*>(block + 1024 + lane * 8);
+    return v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, 0, 0};
+}
+
+template <int FMT, int FA>
+__device__ __forceinline__ void skinny_load(const uint8_t* __restrict__ Xq,
+                                            const uint8_t* __restrict__ Wq, int nb, int j,
+                                            int kblocks, int mb, int lane,
+                                            SkinnyOps<FMT, FA>& op) {
+    using F = Fmt<FMT>;
+    const uint8_t* wblk = Wq + ((size_t)nb * kblocks + j) * F::kWBlock;
+    if constexpr (FMT == kFmtF6) op.w = load_f6_operand(wblk, lane);
+    else op.w = *reinterpret_cast<const uint2*>(wblk + lane * 8);
+#pragma unroll
+    for (int g = 0; g < FA; ++g) {
+        if (g < mb) {
+            const uint8_t* ablk = Xq + ((size_t)g * kblocks + j) * F::kABlock;
+            if constexpr (FMT == kFmtF6) op.a[g] = load_f6_operand(ablk, lane);
+            else if constexpr (FMT == kFmtA8) op.a[g] = *reinterpret_cast<const uint4*>(ablk + lane * 16);
+            else op.a[g] = *reinterpret_cast<const uint2*>(ablk + lane * 8);
+        }
+    }
+}
+
+template <int FMT, int FA>
+__device__ __forceinline__ void skinny_mma(const SkinnyOps<FMT, FA>& op, int mb,
+                                           typename Fmt<FMT>::Acc (&acc)[FA]) {
+    if constexpr (FMT == kFmtF6) {
+#pragma unroll
+        for (int g = 0; g < FA; ++g)
+            if (g < mb)
+                acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    op.w, op.a[g], acc[g], 2, 2, 0, 127, 0, 127);
+    } else {
+        const v4i wf = widen_nibbles(op.w.x, op.w.y);
+#pragma unroll
+        for (int g = 0; g < FA; ++g) {
+            if (g < mb) {
+                v4i af;
+                if constexpr (FMT == kFmtA8)
+                    af = v4i{(int)op.a[g].x, (int)op.a[g].y, (int)op.a[g].z, (int)op.a[g].w};
+                else
+                    af = widen_nibbles(op.a[g].x, op.a[g].y);
+                acc[g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf, af, acc[g], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Substeps per load chunk: every wave keeps two chunks in flight.
+template <int FMT, int FA>
+struct SkinnyChunk {
+    static constexpr int kRegs = (FMT == kFmtF6 ? 8 : 2) +
+                                 FA * (FMT == kFmtF6 ? 8 : (FMT == kFmtA8 ? 4 : 2));
+    static constexpr int D = kRegs <= 12 ? 8 : (kRegs <= 24 ? 4 : 2);
+};
+
+template <int FMT, int FA, bool ACC_OUT>
+__global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
+    const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, const float* __restrict__ comp_a,
+    const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
+    int32_t* __restrict__ acc_out) {
+    using F = Fmt<FMT>;
+    using Acc = typename F::Acc;
+    static_assert(FA * 32 <= kSkinnyThreads, "one thread per row for the row data");
+    // exact integer dot products, summed as int32 (fp32 partials of the
+    // E2M3 path are integers below 2^24 and convert exactly)
+    __shared__ int sum[FA * 32 * kSkinnyPitch];
+    // per-block epilogue operands: w_scale[32], comp_a[S][32], comp_b[S][32]
+    __shared__ float tab[32 + 64 * RUDDER_MAX_STREAMS];
+    __shared__ float rows_rs[FA * 32];
+    __shared__ int rows_s[FA * 32];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int nb = blockIdx.x;                     // 32-channel block
+    const int kblocks = K / F::kKSub;
+    // this workgroup's rows: group blockIdx.y of FA * 32 rows
+    {
+        const int row0 = blockIdx.y * FA * 32;
+        Xq += (size_t)(row0 >> 5) * kblocks * F::kABlock;
+        row_scale += row0;
+        sid += row0;
+        Y += (size_t)row0 * N;
+        if constexpr (ACC_OUT) acc_out += (size_t)row0 * N;
+        M = min(M - row0, FA * 32);
+    }
+    const int mb = (M + 31) >> 5;                  // 32-row blocks present (<= FA)
+
+    for (int i = tid; i < FA * 32 * kSkinnyPitch; i += kSkinnyThreads) sum[i] = 0;
+
+    // epilogue operands: fetched now (in flight with the k loop), written to
+    // LDS after it
+    const int ntab = 32 + 64 * S;
+    auto tab_src = [&](int i) -> const float* {
+        if (i < 32) return w_scale + nb * 32 + i;
+        i -= 32;
+        const int half = i / (32 * S);             // 0: comp_a, 1: comp_b
+        i -= half * 32 * S;
+        return (half ? comp_b : comp_a) + (size_t)(i >> 5) * N + nb * 32 + (i & 31);
+    };
+    const float e_tab0 = tid < ntab ? *tab_src(tid) : 0.0f;
+    const float e_tab1 = tid + kSkinnyThreads < ntab ? *tab_src(tid + kSkinnyThreads) : 0.0f;
+    const float e_rs = tid < M ? row_scale[tid] : 0.0f;
+    const int e_s = tid < M ? min(sid[tid] & (RUDDER_MAX_STREAMS - 1), S - 1) : 0;
+
+    Acc acc[FA];
+#pragma unroll
+    for (int g = 0; g < FA; ++g)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[g][r] = 0;
+
+    // Each wave takes a contiguous range of k-substeps and walks it in chunks
+    // of D substeps; the loads of chunk c+1 are issued before the MFMAs of
+    // chunk c, so two chunks (the whole range for short K) are in flight.
+    constexpr int D = SkinnyChunk<FMT, FA>::D;
+    const int per_wave = (kblocks + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int j0 = wave * per_wave;
+    const int j1 = min(j0 + per_wave, kblocks);
+    SkinnyOps<FMT, FA> ops[2][D];
+    auto load_chunk = [&](int jc, SkinnyOps<FMT, FA>(&buf)[D]) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (jc + d < j1) skinny_load<FMT, FA>(Xq, Wq, nb, jc + d, kblocks, mb, lane, buf[d]);
+    };
+    auto mma_chunk = [&](int jc, const SkinnyOps<FMT, FA>(&buf)[D]) {
+#pragma unroll
+        for (int d = 0; d < D; ++d)
+            if (jc + d < j1) skinny_mma<FMT, FA>(buf[d], mb, acc);
+    };
+    if (j0 < j1) load_chunk(j0, ops[0]);
+    for (int jc = j0; jc < j1; jc += 2 * D) {
+        if (jc + D < j1) load_chunk(jc + D, ops[1]);
+        mma_chunk(jc, ops[0]);
+        if (jc + D < j1) {
+            if (jc + 2 * D < j1) load_chunk(jc + 2 * D, ops[0]);
+            mma_chunk(jc + D, ops[1]);
+        }
+    }
+    if (tid < ntab) tab[tid] = e_tab0;
+    if (tid + kSkinnyThreads < ntab) tab[tid + kSkinnyThreads] = e_tab1;
+    if (tid < FA * 32) {
+        rows_rs[tid] = e_rs;
+        rows_s[tid] = e_s;
+    }
+    __syncthreads();                               // sum tile cleared, operands in LDS
+
+    // partial sums -> LDS tile [row][channel] (row pitch 33 words)
+#pragma unroll
+    for (int g = 0; g < FA; ++g) {
+        if (g < mb) {
+            const int m = g * 32 + (lane & 31);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int n = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                atomicAdd(&sum[m * kSkinnyPitch + n], (int)acc[g][r]);
+            }
+        }
+    }
+    __syncthreads();
+
+    // epilogue: item = (row m, 8-channel group c); 4 items per row
+    for (int item = tid; item < mb * 32 * 4; item += kSkinnyThreads) {
+        const int m = item >> 2;
+        const int c = item & 3;
+        if (m >= M) continue;
+        const int n0 = nb * 32 + c * 8;
+        const int st = rows_s[m];
+        const float rs = rows_rs[m];
+        const float* ws = tab + c * 8;
+        const float* a = tab + 32 + st * 32 + c * 8;
+        const float* b = tab + 32 + 32 * S + st * 32 + c * 8;
+        int v[8];
+        float y[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int w = sum[m * kSkinnyPitch + c * 8 + i];
+            if constexpr (FMT == kFmtF6) v[i] = w;
+            else if constexpr (FMT == kFmtA8) v[i] = w >> 4;
+            else v[i] = w >> 8;
+            y[i] = __builtin_fmaf(a[i], (float)v[i] * (rs * ws[i]), b[i]);
+        }
+        uint4 out;
+        out.x = pack_bf16x2_rne(y[0], y[1]);
+        out.y = pack_bf16x2_rne(y[2], y[3]);
+        out.z = pack_bf16x2_rne(y[4], y[5]);
+        out.w = pack_bf16x2_rne(y[6], y[7]);
+        *reinterpret_cast<uint4*>(Y + (size_t)m * N + n0) = out;
+        if constexpr (ACC_OUT) {
+            *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n0) =
+                make_int4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n0 + 4) =
+                make_int4(v[4], v[5], v[6], v[7]);
+        }
+    }
+}
+
+template <int FMT, int FA, bool ACC_OUT>
+hipError_t launch_skinny(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
+                         int32_t* acc_out, hipStream_t stream) {
+    const unsigned row_groups = (unsigned)((M + FA * 32 - 1) / (FA * 32));
+    hipLaunchKernelGGL((w4_skinny_kernel<FMT, FA, ACC_OUT>), dim3((unsigned)(N / 32), row_groups),
+                       dim3(kSkinnyThreads), 0, stream, xq, row_scale, sid, Wq, w_scale, comp_a,
+                       comp_b, M, N, K, S, Y, acc_out);
+    return hipGetLastError();
 }
 
 template <int FMT, int NS, bool ACC_OUT>
@@ -536,7 +809,6 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
                           int32_t* acc_out, hipStream_t stream) {
     using C = Cfg<FMT, NS>;
     static_assert(C::lds_bytes(1) <= kLdsLimit, "LDS budget");
-    static_assert(C::lds_bytes(RUDDER_MAX_STREAMS) <= 160 * 1024, "LDS budget");
     // the attribute admits the full CU; a call whose tables do not fit the
     // per-workgroup share simply runs fewer workgroups per CU
     static const hipError_t attr = hipFuncSetAttribute(
@@ -556,16 +828,27 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
                       const uint8_t* Wq, const float* w_scale, const float* comp_a,
                       const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                       int32_t* acc_out, hipStream_t stream) {
-    // deepest ring that fits the per-workgroup LDS share with this call's tables
-    constexpr int NS_MAX = FMT == kFmtA4 ? 3 : 2;
-    if constexpr (NS_MAX > 2) {
-        if (Cfg<FMT, NS_MAX>::lds_bytes(S) > kLdsLimit)
-            return launch_variant<FMT, NS_MAX - 1, ACC_OUT>(xq, row_scale, sid, Wq, w_scale,
-                                                            comp_a, comp_b, M, N, K, S, Y,
-                                                            acc_out, stream);
+    // few token rows: the weight-streaming kernel
+    if (M <= kSkinnyMaxM) {
+        if (M <= 64)
+            return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                  comp_b, M, N, K, S, Y, acc_out, stream);
+        return launch_skinny<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
+                                              M, N, K, S, Y, acc_out, stream);
     }
-    return launch_variant<FMT, NS_MAX, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
-                                                M, N, K, S, Y, acc_out, stream);
+    // deepest ring (up to 4 stages) that fits the per-workgroup LDS share
+    // with this call's tables
+#define RUDDER_TRY_NS(NS)                                                                   \
+    if (Cfg<FMT, NS>::lds_bytes(S) <= kLdsLimit)                                            \
+        return launch_variant<FMT, NS, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,    \
+                                                comp_b, M, N, K, S, Y, acc_out, stream);
+    // the two-stage ring fits every stream count
+    static_assert(Cfg<FMT, 2>::lds_bytes(RUDDER_MAX_STREAMS) <= 160 * 1024, "LDS budget");
+    if constexpr (Cfg<FMT, 4>::lds_bytes(1) <= kLdsLimit) { RUDDER_TRY_NS(4) }
+    if constexpr (Cfg<FMT, 3>::lds_bytes(1) <= kLdsLimit) { RUDDER_TRY_NS(3) }
+#undef RUDDER_TRY_NS
+    return launch_variant<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
+                                           N, K, S, Y, acc_out, stream);
 }
 
 }  // namespace

@@ -18,7 +18,9 @@ summed over the four linears, per second, both kernels of each linear
 included); `us_per_step` is the latency of one step.  `roofline` describes
 the kernel that takes the most time per step, timed live with HIP events
 around each of its launches on the launch stream.  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step.
+CPU oracle on a bounded sample of the same step.  `small_m` reports
+action/proprio-sized calls (96 and 192 rows against full-width weights) as
+achieved HBM GB/s, timed as graph replays.
 
 --workload picks another workload (each printed as one JSON line of the
 same form, steps cycling through its step-indexed scale sets).
@@ -73,6 +75,8 @@ def parse_args():
     p.add_argument("--w4a4-codes", choices=["int", "e2m3"], default="e2m3",
                    help="code container of the W4A4 linears (identical outputs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-small-m", action="store_true",
+                   help="skip the few-row (weight-streaming) calls")
     p.add_argument("--no-bf16", action="store_true",
                    help="skip the library comparators (bf16 matmul, int8 GEMM)")
     p.add_argument("--cpu-rows", type=int, default=8384,
@@ -258,6 +262,82 @@ def int8_library_comparator(wl, layers, torch, reps: int = 10):
     return tot * 1e3
 
 
+SMALL_M_CASES = (
+    # name, M, K, N, abits, W4A4 codes: an action/proprio-sized call against
+    # full-width weights (the weights dominate the bytes)
+    ("m96_qkv_h2048_w4a8", 96, 2048, 6144, 8, "int"),
+    ("m192_qkv_h4096_w4a4", 192, 4096, 12288, 4, "e2m3"),
+)
+
+
+def small_m_calls(torch, rudder, w4a4_codes: str, reps: int = 20):
+    """Few-row calls timed as graph replays of `reps` back-to-back calls (a
+    few-µs kernel is otherwise timed by the host's issue rate).  Reports the
+    GEMM kernel alone and quant_act + linear, with the GEMM's algorithmic
+    bytes (packed weights + codes in + bf16 out + scales) per second."""
+    out = {}
+    S = 3
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+    for name, M, K, N, abits, codes_name in SMALL_M_CASES:
+        codes = rudder.CODES_E2M3 if (abits == 4 and (codes_name == "e2m3" and
+                                                      w4a4_codes == "e2m3")) else rudder.CODES_INT
+        X = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+        Wt = (torch.randn(K, N, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+        smooth = torch.ones(K, device="cuda")
+        sid = (torch.arange(M, device="cuda") % S).to(torch.uint8)
+        Wq, ws, inv = rudder.quantize_weights(Wt, smooth, codes)
+        delta = torch.tensor([0.02, 0.03, 0.025], device="cuda")
+        ca = torch.rand(S, N, device="cuda", generator=gen) + 0.5
+        cb = torch.randn(S, N, device="cuda", generator=gen) * 0.01
+        Xq, rs = rudder.quant_act(X, sid, inv, delta, S, abits, codes)
+        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+
+        def gemm():
+            rudder.rudder_linear(Xq, rs, sid, Wq, ws, ca, cb, M, N, K, S, abits, codes, Y)
+
+        def pair():
+            rudder.rudder_quant_act(X, sid, inv, delta, None, None, M, K, S, abits, codes, Xq, rs)
+            gemm()
+
+        res = {}
+        for label, fn in (("gemm", gemm), ("quant_act+gemm", pair)):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                with torch.cuda.graph(g, stream=st):
+                    for _ in range(reps):
+                        fn()
+            torch.cuda.synchronize()
+            g.replay()
+            best = 1e9
+            for _ in range(3):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda.synchronize()
+                e0.record()
+                g.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                best = min(best, e0.elapsed_time(e1) / reps)
+            res[label] = best * 1e3
+        wbytes = 0.75 if codes == rudder.CODES_E2M3 else 0.5
+        abytes = 0.75 if codes == rudder.CODES_E2M3 else abits / 8
+        gemm_bytes = N * K * wbytes + M * K * abytes + 2 * M * N + 4 * N + 8 * S * N + 5 * M
+        gbs = gemm_bytes / (res["gemm"] * 1e-6) / 1e9
+        out[name] = {"M": M, "K": K, "N": N,
+                     "codes": "e2m3" if codes == rudder.CODES_E2M3 else "int",
+                     "gemm_us": round(res["gemm"], 2),
+                     "quant_act_plus_gemm_us": round(res["quant_act+gemm"], 2),
+                     "gemm_bytes": int(gemm_bytes), "gemm_GBps": round(gbs, 1),
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+        del X, Wt, Wq, Xq, Y
+    return out
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -380,6 +460,8 @@ def main():
         i8_us = int8_library_comparator(wl, layers, torch)
         if i8_us is not None:
             out["int8_library_gemm_us_per_step"] = round(i8_us, 1)
+    if not args.no_small_m:
+        out["small_m"] = small_m_calls(torch, rudder, args.w4a4_codes)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.cpu_steps, args.seed)
     print(json.dumps(out), flush=True)

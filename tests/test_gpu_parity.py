@@ -127,6 +127,20 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
 
 
+# Row counts just past a whole number of tile rounds: the tiled kernel takes
+# the rows of the full rounds and the weight-streaming kernel the remainder
+# (8192 + 100 rows x 2048 channels = 520 tiles of 128 x 256 for 512 resident
+# workgroups).  Every row is compared.
+@pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes", [
+    (8292, 128, 2048, 3, 8, False, 40, CODES_INT),
+    (8292, 256, 2048, 3, 4, True, 41, CODES_E2M3),
+    (8292, 128, 2048, 2, 4, False, 42, CODES_INT),
+])
+def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
+    log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")
+    log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
+
+
 @pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3)])
 def test_saturated_codes_at_max_k(abits, codes):
     """K = 65536 (the largest supported) with every weight and activation code

@@ -573,6 +573,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyMaxM = 256;                 // rows handled by the small-M kernel
+constexpr int kSplitMaxWidth = 8192;             // see launch_fmt
 constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 constexpr int kSkinnyPitch = 33;                 // LDS row pitch (words) of the sum tile
 
@@ -824,31 +825,109 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
 }
 
 template <int FMT, bool ACC_OUT>
+hipError_t launch_small(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+                        const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                        const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
+                        int32_t* acc_out, hipStream_t stream) {
+    if (M <= 64)
+        return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
+                                              M, N, K, S, Y, acc_out, stream);
+    return launch_skinny<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
+                                          N, K, S, Y, acc_out, stream);
+}
+
+// Ring depth of the tiled kernel for S streams: the deepest (up to 4 stages)
+// that fits the per-workgroup LDS share with the call's tables.
+template <int FMT>
+int tiled_stages(int S) {
+    // the two-stage ring fits every stream count
+    static_assert(Cfg<FMT, 2>::lds_bytes(RUDDER_MAX_STREAMS) <= 160 * 1024, "LDS budget");
+    if (Cfg<FMT, 4>::lds_bytes(1) <= kLdsLimit && Cfg<FMT, 4>::lds_bytes(S) <= kLdsLimit)
+        return 4;
+    if (Cfg<FMT, 3>::lds_bytes(1) <= kLdsLimit && Cfg<FMT, 3>::lds_bytes(S) <= kLdsLimit)
+        return 3;
+    return 2;
+}
+
+template <int FMT>
+size_t tiled_lds_bytes(int ns, int S) {
+    return ns == 4 ? Cfg<FMT, 4>::lds_bytes(S)
+                   : (ns == 3 ? Cfg<FMT, 3>::lds_bytes(S) : Cfg<FMT, 2>::lds_bytes(S));
+}
+
+template <int FMT, bool ACC_OUT>
+hipError_t launch_tiled(int ns, const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+                        const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                        const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
+                        int32_t* acc_out, hipStream_t stream) {
+    if constexpr (Cfg<FMT, 4>::lds_bytes(1) <= kLdsLimit)
+        if (ns == 4)
+            return launch_variant<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                   comp_b, M, N, K, S, Y, acc_out, stream);
+    if constexpr (Cfg<FMT, 3>::lds_bytes(1) <= kLdsLimit)
+        if (ns == 3)
+            return launch_variant<FMT, 3, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                   comp_b, M, N, K, S, Y, acc_out, stream);
+    return launch_variant<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
+                                           N, K, S, Y, acc_out, stream);
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+template <int FMT, bool ACC_OUT>
 hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                       const uint8_t* Wq, const float* w_scale, const float* comp_a,
                       const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                       int32_t* acc_out, hipStream_t stream) {
     // few token rows: the weight-streaming kernel
-    if (M <= kSkinnyMaxM) {
-        if (M <= 64)
-            return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                  comp_b, M, N, K, S, Y, acc_out, stream);
-        return launch_skinny<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
-                                              M, N, K, S, Y, acc_out, stream);
+    if (M <= kSkinnyMaxM)
+        return launch_small<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N,
+                                          K, S, Y, acc_out, stream);
+    const int ns = tiled_stages<FMT>(S);
+    // Ragged last round: when the tiles fill whole rounds of resident
+    // workgroups except for a few rows (at most kSkinnyMaxM), the tiled
+    // kernel takes the rows of the full rounds and the weight-streaming
+    // kernel the rest, instead of a nearly empty extra round of tiles.  The
+    // streaming kernel reads the weights once per 128-row group, so this
+    // pays only for narrow layers: groups * N <= kSplitMaxWidth (measured on
+    // 2048-, 4096- and 8192-wide layers, where it saves 5-25%; on 12288- and
+    // 16384-wide layers the partial round is cheaper).
+    const int tiles_n = (N + BN - 1) / BN;
+    const int tiles = ((M + BM - 1) / BM) * tiles_n;
+    const int per_cu = (int)((160 * 1024) / tiled_lds_bytes<FMT>(ns, S));
+    const int slots = device_cus() * (per_cu < kBlocksPerCU ? per_cu : kBlocksPerCU);
+    const int full = slots > 0 ? tiles / slots : 0;
+    if (full >= 1 && tiles % slots != 0) {
+        const int m_main = (full * slots / tiles_n) * BM;
+        const int tail = M - m_main;
+        const int groups = (tail + 127) / 128;
+        if (m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && groups * N <= kSplitMaxWidth) {
+            const hipError_t e = launch_tiled<FMT, ACC_OUT>(ns, xq, row_scale, sid, Wq, w_scale,
+                                                            comp_a, comp_b, m_main, N, K, S, Y,
+                                                            acc_out, stream);
+            if (e != hipSuccess) return e;
+            const size_t a_off = (size_t)(m_main / 32) * (K / Fmt<FMT>::kKSub) * Fmt<FMT>::kABlock;
+            return launch_small<FMT, ACC_OUT>(
+                xq + a_off, row_scale + m_main, sid + m_main, Wq, w_scale, comp_a, comp_b, tail,
+                N, K, S, Y + (size_t)m_main * N,
+                ACC_OUT ? acc_out + (size_t)m_main * N : acc_out, stream);
+        }
     }
-    // deepest ring (up to 4 stages) that fits the per-workgroup LDS share
-    // with this call's tables
-#define RUDDER_TRY_NS(NS)                                                                   \
-    if (Cfg<FMT, NS>::lds_bytes(S) <= kLdsLimit)                                            \
-        return launch_variant<FMT, NS, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,    \
-                                                comp_b, M, N, K, S, Y, acc_out, stream);
-    // the two-stage ring fits every stream count
-    static_assert(Cfg<FMT, 2>::lds_bytes(RUDDER_MAX_STREAMS) <= 160 * 1024, "LDS budget");
-    if constexpr (Cfg<FMT, 4>::lds_bytes(1) <= kLdsLimit) { RUDDER_TRY_NS(4) }
-    if constexpr (Cfg<FMT, 3>::lds_bytes(1) <= kLdsLimit) { RUDDER_TRY_NS(3) }
-#undef RUDDER_TRY_NS
-    return launch_variant<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
-                                           N, K, S, Y, acc_out, stream);
+    return launch_tiled<FMT, ACC_OUT>(ns, xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N,
+                                      K, S, Y, acc_out, stream);
 }
 
 }  // namespace

@@ -20,7 +20,7 @@ import numpy as np
 __all__ = [
     "build", "load", "bf16_to_f32", "f32_to_bf16", "inv_smooth", "quantize_weights",
     "dynamic_scales", "quant_act", "pack_int4", "unpack_int4", "int_gemm", "epilogue",
-    "linear", "num_threads", "OracleError",
+    "linear", "gelu_bf16", "linear_gelu_quant", "num_threads", "OracleError",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -204,6 +204,29 @@ def epilogue(acc: np.ndarray, row_scale: np.ndarray, stream_id: np.ndarray,
     _check(load().oracle_epilogue(_p(acc), _p(rs), _p(sid), _p(ws), _p(ca), _p(cb),
                                   M, N, S, _p(Y)), "epilogue")
     return Y
+
+
+def gelu_bf16(bits: np.ndarray) -> np.ndarray:
+    """GELU between the MLP projections, kept in BF16 (SteerQuant App. D):
+    the exact erf form of a bf16 input, fp64, rounded to fp32 then bf16.
+    Pinned by: scipy's independent erfc over all 65536 inputs, closed-form
+    values, the identity gelu(x) - gelu(-x) = x, the tails."""
+    b = _c(bits, np.uint16)
+    out = np.empty_like(b)
+    load().oracle_gelu_bf16(_p(b), _p(out), ctypes.c_long(b.size))
+    return out
+
+
+def linear_gelu_quant(X, stream_id, codes_w, w_scale, inv_s, delta, comp_a, comp_b, S, abits,
+                      next_inv_s, next_delta, next_abits):
+    """Up-projection, GELU in BF16 and the next (down) layer's activation
+    quantizer, as one fused call would compute them (SteerQuant §4.4: only
+    integer activations and row scales travel between kernels; App. D: GELU
+    stays BF16).  The composition of linear, gelu_bf16 and quant_act.
+    Returns (next act codes, next row_scale)."""
+    _, _, _, Y = linear(X, stream_id, codes_w, w_scale, inv_s, delta, comp_a, comp_b, S, abits)
+    G = gelu_bf16(Y)
+    return quant_act(G, stream_id, next_inv_s, next_delta, S, next_abits)
 
 
 def linear(X, stream_id, codes_w, w_scale, inv_s, delta, comp_a, comp_b, S, abits):

@@ -280,6 +280,31 @@ int oracle_epilogue(const int32_t* acc, const float* row_scale, const uint8_t* s
     return ORACLE_OK;
 }
 
+/* ---- GELU between the MLP projections (SteerQuant App. D: GELU stays BF16) */
+
+/*
+ * The exact (erf) form on a bf16 input, gelu(x) = x * Phi(x), evaluated in
+ * fp64 as 0.5 * x * erfc(-x / sqrt(2)) (erfc keeps the tail accurate for
+ * negative x), then rounded to fp32 and from fp32 to bf16, both
+ * round-to-nearest-even.  Non-finite inputs: NaN -> quiet NaN of the same
+ * sign, +inf -> +inf, -inf -> -0.
+ */
+static uint16_t gelu_bf16_one(uint16_t h) {
+    const uint32_t exp_bits = (h >> 7) & 0xFFu;
+    const uint16_t sign = h & 0x8000u;
+    if (exp_bits == 0xFFu) {
+        if (h & 0x7Fu) return (uint16_t)(sign | 0x7FC0u);   /* NaN */
+        return sign ? (uint16_t)0x8000u : (uint16_t)0x7F80u; /* -inf -> -0, +inf -> +inf */
+    }
+    const double x = (double)bf16_to_float(h);
+    const double g = 0.5 * x * erfc(-x * 0.70710678118654752440);
+    return float_to_bf16_rne((float)g);
+}
+
+void oracle_gelu_bf16(const uint16_t* in, uint16_t* out, long n) {
+    for (long i = 0; i < n; ++i) out[i] = gelu_bf16_one(in[i]);
+}
+
 /* Thread count OpenMP will use (reported by the CPU baseline). */
 int oracle_num_threads(void) {
 #ifdef _OPENMP

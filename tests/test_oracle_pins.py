@@ -467,3 +467,103 @@ def test_pack_roundtrip_random(orc):
     rng = np.random.default_rng(12)
     c = rng.integers(-8, 8, (33, 256)).astype(np.int8)
     assert np.array_equal(orc.unpack_int4(orc.pack_int4(c), 256), c)
+
+
+# ---------------------------------------------------------------------------
+# GELU between the MLP projections (kept in BF16: SteerQuant App. D), for the
+# fused up-projection -> GELU -> down-layer quantizer path
+# ---------------------------------------------------------------------------
+
+def _all_bf16():
+    return np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+def test_gelu_matches_scipy_every_finite_input(orc):
+    """An independent erfc (scipy's) in fp64 gives the same bf16 result for
+    every finite bf16 input."""
+    from scipy.special import erfc
+    b = _all_bf16()
+    x = orc.bf16_to_f32(b).astype(np.float64)
+    fin = np.isfinite(x)
+    g64 = 0.5 * x[fin] * erfc(-x[fin] / np.sqrt(2.0))
+    ref = orc.f32_to_bf16(g64.astype(np.float32))
+    got = orc.gelu_bf16(b)[fin]
+    assert np.array_equal(got, ref), int((got != ref).sum())
+
+
+def test_gelu_closed_form_values(orc):
+    """gelu(x) = x * Phi(x) at points where Phi has textbook values."""
+    phi = {1.0: 0.8413447460685429, 2.0: 0.9772498680518208, 0.5: 0.6914624612740131}
+    for x, p in phi.items():
+        for sx in (x, -x):
+            want = sx * (p if sx > 0 else 1.0 - p)
+            wb = orc.f32_to_bf16(np.array([want], np.float32))
+            got = orc.gelu_bf16(orc.f32_to_bf16(np.array([sx], np.float32)))
+            assert got[0] == wb[0], (sx, hex(int(got[0])), hex(int(wb[0])))
+
+
+def test_gelu_odd_identity(orc):
+    """gelu(x) - gelu(-x) = x exactly; after the two bf16 roundings the
+    difference stays within half an ulp of each output."""
+    b = _all_bf16()
+    x = orc.bf16_to_f32(b).astype(np.float64)
+    sel = np.isfinite(x) & (np.abs(x) > 1e-30) & (np.abs(x) < 1e30)
+    bx = b[sel]
+    gp = orc.bf16_to_f32(orc.gelu_bf16(bx)).astype(np.float64)
+    gm = orc.bf16_to_f32(orc.gelu_bf16(bx ^ np.uint16(0x8000))).astype(np.float64)
+    xx = x[sel]
+
+    def half_ulp(v):
+        e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+        return 2.0 ** (e - 8)
+    assert np.all(np.abs(gp - gm - xx) <= half_ulp(gp) + half_ulp(gm) + 1e-300)
+
+
+def test_gelu_tails_and_special_values(orc):
+    b = _all_bf16()
+    x = orc.bf16_to_f32(b).astype(np.float64)
+    g = orc.gelu_bf16(b)
+    gv = orc.bf16_to_f32(g).astype(np.float64)
+    fin = np.isfinite(x)
+    # large positive inputs pass through unchanged (x * Q(x) < half an ulp)
+    big = fin & (x >= 4.0)
+    assert np.array_equal(g[big], b[big])
+    # negative inputs give non-positive outputs, bounded below by the minimum
+    # of x * Phi(x) (about -0.17 near x = -0.75)
+    neg = fin & (x < 0)
+    assert np.all(gv[neg] <= 0) and np.all(gv[neg] >= -0.1702)
+    # zeros keep their sign; far negative inputs underflow to -0
+    assert orc.gelu_bf16(np.array([0x0000, 0x8000], np.uint16)).tolist() == [0x0000, 0x8000]
+    far = fin & (x < -14.0)
+    assert np.all(g[far] == 0x8000)
+    # non-finite inputs
+    sp = orc.gelu_bf16(np.array([0x7F80, 0xFF80, 0x7FC0, 0xFFC1], np.uint16)).tolist()
+    assert sp == [0x7F80, 0x8000, 0x7FC0, 0xFFC0]
+
+
+def test_linear_gelu_quant_is_the_composition(orc):
+    """The fused reference is the unfused chain: the layer's bf16 output,
+    GELU, then the next layer's quantizer on it (each piece pinned above)."""
+    rng = np.random.default_rng(31)
+    M, K, N, S = 40, 64, 96, 3
+    X = orc.f32_to_bf16(rng.standard_normal((M, K)).astype(np.float32))
+    W = orc.f32_to_bf16((rng.standard_normal((K, N)) * 0.05).astype(np.float32))
+    s = rng.uniform(0.5, 2.0, K).astype(np.float32)
+    sid = (np.arange(M) % S).astype(np.uint8)
+    inv = orc.inv_smooth(s)
+    qw, ws = orc.quantize_weights(W, s)
+    delta = np.array([0.02, 0.03, 0.025], np.float32)
+    a = rng.uniform(0.9, 1.1, (S, N)).astype(np.float32)
+    bb = (rng.standard_normal((S, N)) * 0.01).astype(np.float32)
+    ninv = rng.uniform(0.5, 2.0, N).astype(np.float32)
+    nd = np.array([0.01, 0.02, 0.015], np.float32)
+    q2, rs2 = orc.linear_gelu_quant(X, sid, qw, ws, inv, delta, a, bb, S, 8, ninv, nd, 4)
+    _, _, _, Y = orc.linear(X, sid, qw, ws, inv, delta, a, bb, S, 8)
+    G = orc.gelu_bf16(Y)
+    # the next quantizer, written out from its definition
+    u = orc.bf16_to_f32(G) * ninv[None, :]
+    ia = np.array([np.float32(1.0 / np.float64(d)) for d in nd], np.float32)
+    v = (u * ia[sid][:, None]).astype(np.float32)
+    want = np.rint(np.clip(v, -7, 7)).astype(np.int8)
+    assert np.array_equal(q2, want)
+    assert np.array_equal(rs2, nd[sid])

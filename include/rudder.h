@@ -204,6 +204,51 @@ rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint
                               int M, int N, int K, int S, int abits, int codes,
                               uint16_t* Y, int32_t* acc_out, void* stream);
 
+/*
+ * MLP up-projection with GELU and the down layer's activation quantizer fused
+ * into the epilogue (SteerQuant §4.4: only integer activations and row scales
+ * travel between kernels; App. D: GELU stays in BF16).  The bf16 output of
+ * the up-projection never reaches HBM.
+ *
+ * Per element this computes exactly what the unfused chain computes:
+ *   Y  = the bf16 output rudder_linear would write (same arguments);
+ *   G  = gelu(Y): the exact (erf) form x * Phi(x) of the bf16 value Y,
+ *        evaluated in fp64 and rounded to fp32, then to bf16 (RNE both
+ *        times) -- rudder_gelu_bf16 applies the same function;
+ *   then rudder_quant_act in static mode on G (as the down layer's input,
+ *   K' = N channels) with next_inv_smooth and next_act_scale.
+ *
+ *   Xq ... codes    as for rudder_linear (the up-projection; M >= 0)
+ *   next_inv_smooth fp32 [N]: the down layer's inverse smoothing factors
+ *   next_act_scale  fp32 [S]: the down layer's step sizes D'[s] at this step
+ *   next_abits      4 or 8;  next_codes  RUDDER_CODES_INT, or
+ *                   RUDDER_CODES_E2M3 (next_abits = 4, N a multiple of 64)
+ *   next_Xq         out: rudder_packed_act_bytes(M, N, next_abits,
+ *                   next_codes) bytes, the down layer's packed activations
+ *                   (padding rows 0)
+ *   next_row_scale  out: fp32 [M] = D'[stream_id[m]]
+ * Errors: those of rudder_linear, plus INVALID_ARG for a null
+ * next_inv_smooth/next_act_scale/next_Xq/next_row_scale, next_abits not 4 or
+ * 8, an unknown next container or E2M3 with next_abits = 8 or N % 64 != 0,
+ * next_inv_smooth/next_Xq not 16-byte aligned.
+ */
+rudder_status_t rudder_linear_gelu_quant(const void* Xq, const float* row_scale,
+                                         const uint8_t* stream_id, const uint8_t* Wq,
+                                         const float* w_scale, const float* comp_a,
+                                         const float* comp_b, int M, int N, int K, int S,
+                                         int abits, int codes, const float* next_inv_smooth,
+                                         const float* next_act_scale, int next_abits,
+                                         int next_codes, void* next_Xq, float* next_row_scale,
+                                         void* stream);
+
+/*
+ * The GELU of rudder_linear_gelu_quant applied elementwise to n bf16 values
+ * (device buffers; in and out may alias).  A table over the 65536 bf16
+ * patterns: NaN -> quiet NaN of the same sign, +inf -> +inf, -inf -> -0.
+ * Errors: INVALID_ARG for null in/out with n > 0.
+ */
+rudder_status_t rudder_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, void* stream);
+
 /* Static string naming a status code. */
 const char* rudder_status_string(rudder_status_t status);
 

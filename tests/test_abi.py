@@ -23,7 +23,7 @@ def lib():
 def header_functions():
     text = open(os.path.join(ROOT, "include", "rudder.h")).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rudder_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(rudder_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol(lib):
@@ -190,6 +190,38 @@ def test_e2m3_layout_roundtrip_and_slots():
     for t in range(32):
         field = (bits >> (6 * t)) & 0x3F
         assert e2m3_value(np.array([field]))[0] == c[37, 160 + t]
+
+
+def _gelu_quant(lib, **kw):
+    args = dict(Xq=P, rs=P, sid=P, Wq=P, ws=P, a=P, b=P, M=64, N=256, K=256, S=3, abits=4,
+                codes=0, ninv=P, nd=P, nabits=4, ncodes=0, nxq=P, nrs=P)
+    args.update(kw)
+    return lib.rudder_linear_gelu_quant(
+        args["Xq"], args["rs"], args["sid"], args["Wq"], args["ws"], args["a"], args["b"],
+        args["M"], args["N"], args["K"], args["S"], args["abits"], args["codes"], args["ninv"],
+        args["nd"], args["nabits"], args["ncodes"], args["nxq"], args["nrs"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(ninv=None), 1), (dict(nd=None), 1), (dict(nxq=None), 1), (dict(nrs=None), 1),
+    (dict(Wq=None), 1), (dict(nabits=5), 1), (dict(ncodes=2), 1),
+    (dict(ncodes=1, nabits=8), 1), (dict(ncodes=1, N=96), 1), (dict(nxq=P + 4), 1),
+    (dict(ninv=P + 8), 1), (dict(N=48), 1), (dict(S=9), 1), (dict(K=96), 2),
+    (dict(codes=1, abits=8), 1),
+])
+def test_linear_gelu_quant_rejects(lib, kw, status):
+    assert _gelu_quant(lib, **kw) == status
+    assert len(lib.rudder_last_error()) > 0
+
+
+def test_linear_gelu_quant_m0_is_noop(lib):
+    assert _gelu_quant(lib, M=0) == 0
+
+
+def test_gelu_bf16_validation(lib):
+    assert lib.rudder_gelu_bf16(None, None, 0, None) == 0
+    assert lib.rudder_gelu_bf16(None, P, 10, None) == 1
+    assert lib.rudder_gelu_bf16(P, None, 10, None) == 1
 
 
 def test_misaligned_rejected(lib):

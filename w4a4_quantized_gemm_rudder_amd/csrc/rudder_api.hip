@@ -127,12 +127,15 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
                     f);
 }
 
-rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint8_t* stream_id,
-                              const uint8_t* Wq, const float* w_scale, const float* comp_a,
-                              const float* comp_b, int M, int N, int K, int S, int abits,
-                              int codes, uint16_t* Y, int32_t* acc_out, void* stream) {
-    const char* f = "rudder_linear";
-    if (!Xq || !row_scale || !stream_id || !Wq || !w_scale || !comp_a || !comp_b || !Y)
+namespace {
+
+// Checks shared by rudder_linear and rudder_linear_gelu_quant (the output
+// pointers are checked by the callers).
+rudder_status_t check_linear(const char* f, const void* Xq, const float* row_scale,
+                             const uint8_t* stream_id, const uint8_t* Wq, const float* w_scale,
+                             const float* comp_a, const float* comp_b, int M, int N, int K,
+                             int S, int abits, int codes) {
+    if (!Xq || !row_scale || !stream_id || !Wq || !w_scale || !comp_a || !comp_b)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
     if (M < 0 || N <= 0 || K <= 0)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: M=%d must be >= 0, N=%d and K=%d > 0", f, M, N,
@@ -147,18 +150,76 @@ rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint
     if (codes == RUDDER_CODES_E2M3 && abits != 4)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: E2M3 codes need abits=4 (abits=%d)", f, abits);
     if (misaligned(Xq) || misaligned(Wq) || misaligned(w_scale) || misaligned(comp_a) ||
-        misaligned(comp_b) || misaligned(Y) || misaligned(acc_out))
-        return fail(RUDDER_ERR_INVALID_ARG, "%s: Xq, Wq, w_scale, comp_a, comp_b, Y and acc_out "
-                    "must be 16-byte aligned", f);
+        misaligned(comp_b))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: Xq, Wq, w_scale, comp_a and comp_b must be "
+                    "16-byte aligned", f);
     if (K % 128)
         return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d is not a multiple of 128", f, K);
     if (K > RUDDER_MAX_K)
         return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
+    return RUDDER_OK;
+}
+
+}  // namespace
+
+rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint8_t* stream_id,
+                              const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                              const float* comp_b, int M, int N, int K, int S, int abits,
+                              int codes, uint16_t* Y, int32_t* acc_out, void* stream) {
+    const char* f = "rudder_linear";
+    if (!Y) return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (misaligned(Y) || misaligned(acc_out))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: Y and acc_out must be 16-byte aligned", f);
+    const rudder_status_t st = check_linear(f, Xq, row_scale, stream_id, Wq, w_scale, comp_a,
+                                            comp_b, M, N, K, S, abits, codes);
+    if (st != RUDDER_OK) return st;
     if (M == 0) return ok();
     return from_hip(rudder::launch_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b,
                                           M, N, K, S, abits, codes, Y, acc_out,
                                           static_cast<hipStream_t>(stream)),
                     f);
+}
+
+rudder_status_t rudder_linear_gelu_quant(const void* Xq, const float* row_scale,
+                                         const uint8_t* stream_id, const uint8_t* Wq,
+                                         const float* w_scale, const float* comp_a,
+                                         const float* comp_b, int M, int N, int K, int S,
+                                         int abits, int codes, const float* next_inv_smooth,
+                                         const float* next_act_scale, int next_abits,
+                                         int next_codes, void* next_Xq, float* next_row_scale,
+                                         void* stream) {
+    const char* f = "rudder_linear_gelu_quant";
+    if (!next_inv_smooth || !next_act_scale || !next_Xq || !next_row_scale)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (next_abits != 4 && next_abits != 8)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: next_abits=%d must be 4 or 8", f, next_abits);
+    if (next_codes != RUDDER_CODES_INT && next_codes != RUDDER_CODES_E2M3)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, next_codes);
+    if (next_codes == RUDDER_CODES_E2M3 && (next_abits != 4 || N % 64))
+        return fail(RUDDER_ERR_INVALID_ARG,
+                    "%s: E2M3 next codes need next_abits=4 and N a multiple of 64 (%d, N=%d)", f,
+                    next_abits, N);
+    if (misaligned(next_inv_smooth) || misaligned(next_Xq))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: next_inv_smooth and next_Xq must be 16-byte "
+                    "aligned", f);
+    const rudder_status_t st = check_linear(f, Xq, row_scale, stream_id, Wq, w_scale, comp_a,
+                                            comp_b, M, N, K, S, abits, codes);
+    if (st != RUDDER_OK) return st;
+    if (M == 0) return ok();
+    const rudder::NextLayerQuant next{next_inv_smooth, next_act_scale,
+                                      static_cast<uint8_t*>(next_Xq), next_row_scale, next_abits,
+                                      next_codes};
+    return from_hip(rudder::launch_linear_gelu_quant(Xq, row_scale, stream_id, Wq, w_scale,
+                                                     comp_a, comp_b, M, N, K, S, abits, codes,
+                                                     next, static_cast<hipStream_t>(stream)),
+                    f);
+}
+
+rudder_status_t rudder_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, void* stream) {
+    const char* f = "rudder_gelu_bf16";
+    if (n == 0) return ok();
+    if (!in || !out) return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    return from_hip(rudder::launch_gelu_bf16(in, out, n, static_cast<hipStream_t>(stream)), f);
 }
 
 const char* rudder_status_string(rudder_status_t status) {

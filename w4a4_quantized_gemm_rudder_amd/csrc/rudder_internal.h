@@ -33,6 +33,23 @@ hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* 
                          const float* comp_b, int M, int N, int K, int S, int abits, int codes,
                          uint16_t* Y, int32_t* acc_out, hipStream_t stream);
 
+// The down layer's quantizer, fused into the up-projection epilogue.
+struct NextLayerQuant {
+    const float* inv_smooth;   // [N]
+    const float* delta;        // [S]
+    uint8_t* xq;               // packed codes of the down layer's input
+    float* row_scale;          // [M]
+    int abits;
+    int codes;
+};
+
+hipError_t launch_linear_gelu_quant(const void* Xq, const float* row_scale, const uint8_t* sid,
+                                    const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                                    const float* comp_b, int M, int N, int K, int S, int abits,
+                                    int codes, const NextLayerQuant& next, hipStream_t stream);
+
+hipError_t launch_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------

@@ -56,6 +56,19 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kXcds = 8;
 constexpr int kGroupM = 8;       // m-tiles per tile group (L2 reuse of weight panels)
 
+// GELU of every bf16 pattern (the exact erf form, rounded to fp32 then bf16),
+// written at build time by gelu_table_gen.cpp.
+__device__ const uint16_t kGeluBf16[65536] = {
+#include "gelu_table.inc"
+};
+
+// Epilogue modes: the bf16 output, or GELU of it quantized as the next
+// layer's input (int8 codes, split-nibble int4 codes, E2M3 codes).
+constexpr int kEpiBf16 = 0;
+constexpr int kEpiQ8 = 1;
+constexpr int kEpiQ4 = 2;
+constexpr int kEpiE2M3 = 3;
+
 // Code formats of the GEMM.
 constexpr int kFmtA8 = 0;        // int8 activations, int4 weights (int8 MFMA)
 constexpr int kFmtA4 = 1;        // int4 activations and weights (int8 MFMA)
@@ -136,7 +149,9 @@ struct Cfg {
     // Per-tile epilogue tables (w_scale, comp_a[S], comp_b[S] for the tile's
     // 256 channels, 1 KiB each) live after both the ring and the bf16 tile.
     static constexpr int kTableOffset = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
-    static constexpr int lds_bytes(int S) { return kTableOffset + (1 + 2 * S) * 1024; }
+    static constexpr int lds_bytes(int S, int extra_rows = 0) {
+        return kTableOffset + (1 + 2 * S + extra_rows) * 1024;
+    }
 };
 
 // LDS per workgroup: the 160 KiB of a gfx950 CU shared by kBlocksPerCU.
@@ -312,13 +327,13 @@ __device__ __forceinline__ int acc_value(const typename Fmt<FMT>::Acc& a, int r)
     else return a[r] >> 8;
 }
 
-template <int FMT, int NS, bool ACC_OUT>
+template <int FMT, int NS, bool ACC_OUT, int EPI>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
     const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
-    int32_t* __restrict__ acc_out, int tiles_m, int tiles_n) {
+    int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, NextLayerQuant nx) {
     using C = Cfg<FMT, NS>;
     using F = Fmt<FMT>;
     constexpr int L = C::kLoads;
@@ -359,7 +374,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     if constexpr (!kLateRowData) fetch_row_data();
 
     // ---- epilogue tables -> LDS (one KiB per table row, one wave each) ----
-    // row 0: w_scale, rows 1..S: comp_a[s], rows S+1..2S: comp_b[s], each for
+    // row 0: w_scale, rows 1..S: comp_a[s], rows S+1..2S: comp_b[s] (and, when
+    // the epilogue quantizes for the next layer, row 2S+1: its inv_smooth), each for
     // channels n_tile0 .. n_tile0 + 255 (a tile narrower than 256 channels
     // reads past its last channel only within the same row of the table
     // when N >= 256; narrower matrices clamp the window to the last 256).
@@ -368,10 +384,12 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         const int nwin = N >= BN ? min(n_tile0, N - BN) : 0;
         const int cols = N >= BN ? BN : N;                   // columns present in the window
         const int per_lane = cols * 4 / 64;                  // bytes per lane (16 when cols = 256)
-        for (int r = uwave; r < 1 + 2 * S; r += kWaves) {
+        const int rows = 1 + 2 * S + (EPI != kEpiBf16 ? 1 : 0);
+        for (int r = uwave; r < rows; r += kWaves) {
             const float* src = r == 0 ? w_scale
                              : (r <= S ? comp_a + (size_t)(r - 1) * N
-                                       : comp_b + (size_t)(r - 1 - S) * N);
+                                       : (r <= 2 * S ? comp_b + (size_t)(r - 1 - S) * N
+                                                     : nx.inv_smooth));
             const uint32_t dst = lds_base + C::kTableOffset + r * 1024;
             if (per_lane == 16) {
                 load_lds16(src + nwin, lane * 16, __builtin_amdgcn_readfirstlane(dst));
@@ -499,6 +517,14 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     auto swz = [](int r) { return kRowChunks == 8 ? ((r >> 1) & 7) : (r & 15); };
     __syncthreads();                                   // ring no longer read
     const float* tab = reinterpret_cast<const float*>(lds + C::kTableOffset);
+    // next-layer quantizer (code epilogues): reciprocal step per row, Qa
+    constexpr float kQNext = EPI == kEpiQ8 ? 127.0f : 7.0f;
+    constexpr int kCodeRowBytes = FW * 32;                     // one byte per channel
+    float next_ia[FA];
+    if constexpr (EPI != kEpiBf16) {
+#pragma unroll
+        for (int g = 0; g < FA; ++g) next_ia[g] = step_reciprocal(nx.delta[row_stream[g]]);
+    }
     const int tab_shift = tile_n * BN - (N >= BN ? min(n_tile0, N - BN) : 0);
     uint8_t* wstage = lds + wave * (kWaveRows * kWaveRowBytes);
 #pragma unroll
@@ -527,8 +553,31 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                 packed.x = pack_bf16x2_rne(y0, y1);
                 packed.y = pack_bf16x2_rne(y2, y3);
                 const int r = g * 32 + (lane & 31);
-                *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes + ((chunk ^ swz(r)) * 16) +
-                                          (lane >> 5) * 8) = packed;
+                if constexpr (EPI == kEpiBf16) {
+                    *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes + ((chunk ^ swz(r)) * 16) +
+                                              (lane >> 5) * 8) = packed;
+                } else {
+                    // GELU of the bf16 values, then the next layer's quantizer:
+                    // u = gelu * inv_smooth'[n]; q = rne(clamp(u * (1/D'[s])))
+                    const float4 ni =
+                        *reinterpret_cast<const float4*>(tab + 256 * (1 + 2 * S) + ti);
+                    const float g0 = bf16_bits_to_float(kGeluBf16[packed.x & 0xFFFFu]);
+                    const float g1 = bf16_bits_to_float(kGeluBf16[packed.x >> 16]);
+                    const float g2 = bf16_bits_to_float(kGeluBf16[packed.y & 0xFFFFu]);
+                    const float g3 = bf16_bits_to_float(kGeluBf16[packed.y >> 16]);
+                    const float ia = next_ia[g];
+                    const uint32_t word =
+                        ((uint32_t)quantize_clamped((g0 * ni.x) * ia, kQNext) & 0xFFu) |
+                        (((uint32_t)quantize_clamped((g1 * ni.y) * ia, kQNext) & 0xFFu) << 8) |
+                        (((uint32_t)quantize_clamped((g2 * ni.z) * ia, kQNext) & 0xFFu) << 16) |
+                        (((uint32_t)quantize_clamped((g3 * ni.w) * ia, kQNext) & 0xFFu) << 24);
+                    // code staging: row r of the wave, 64 one-byte codes, 16-byte
+                    // chunk k16 stored at chunk k16 ^ (r & 3)
+                    *reinterpret_cast<uint32_t*>(
+                        wstage + r * kCodeRowBytes +
+                        (((f * 2 + (q >> 1)) ^ (r & 3)) * 16) + 8 * (q & 1) + 4 * (lane >> 5)) =
+                        word;
+                }
                 if constexpr (ACC_OUT) {
                     const int m = tile_m * BM + wm * kWaveRows + r;
                     const int n = tile_n * BN + nl;
@@ -541,6 +590,73 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         // keep the accumulator reads of one fragment column together
         // (bounds the registers the epilogue needs)
         __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (EPI != kEpiBf16) {
+        // 2'. the next layer's packed codes from the staged bytes (this wave's
+        //     128 rows x 64 channels; rows M .. ceil32(M) - 1 get code 0) and
+        //     its row scales
+        const int m0 = tile_m * BM + wm * kWaveRows;
+        const int n0w = tile_n * BN + wn * (FW * 32);          // wave's first channel
+        const int mpad = (M + 31) & ~31;
+        if (tile_n == 0 && wn == 0 && lane < 32) {
+#pragma unroll
+            for (int g = 0; g < FA; ++g) {
+                const int m = m0 + g * 32 + lane;
+                if (m < M) nx.row_scale[m] = nx.delta[row_stream[g]];
+            }
+        }
+        if (n0w >= N) return;
+        if constexpr (EPI == kEpiE2M3) {
+            // one 32 x 64 block per 32 rows: lane -> (row, 32-channel half)
+            const int half = lane >> 5;
+#pragma unroll
+            for (int rb = 0; rb < FA; ++rb) {
+                const int rr = rb * 32 + (lane & 31);
+                const int m = m0 + rr;
+                if (m >= mpad) continue;
+                const uint4 lo = *reinterpret_cast<const uint4*>(
+                    wstage + rr * kCodeRowBytes + (((2 * half) ^ (rr & 3)) * 16));
+                const uint4 hi = *reinterpret_cast<const uint4*>(
+                    wstage + rr * kCodeRowBytes + (((2 * half + 1) ^ (rr & 3)) * 16));
+                const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+                int c[32];
+#pragma unroll
+                for (int t = 0; t < 32; ++t)
+                    c[t] = m < M ? (int)(int8_t)((w[t >> 2] >> (8 * (t & 3))) & 0xFFu) : 0;
+                uint32_t d[6];
+                pack_e2m3x32(c, d);
+                uint8_t* blk = nx.xq + e2m3_block_offset(m, n0w, N);
+                const int slot = e2m3_slot(m, n0w + 32 * half);
+                *reinterpret_cast<uint4*>(blk + slot * 16) = make_uint4(d[0], d[1], d[2], d[3]);
+                *reinterpret_cast<uint2*>(blk + 1024 + slot * 8) = make_uint2(d[4], d[5]);
+            }
+        } else {
+            // 16-code slots: lane -> (row, 16-channel group) in each 32 x 32 block
+#pragma unroll
+            for (int rb = 0; rb < FA; ++rb) {
+#pragma unroll
+                for (int kc = 0; kc < FW; ++kc) {
+                    const int rr = rb * 32 + (lane & 31);
+                    const int k16 = 2 * kc + (lane >> 5);          // 16-channel group
+                    const int m = m0 + rr;
+                    const int n = n0w + 16 * k16;
+                    if (m >= mpad || n >= N) continue;
+                    uint4 v = *reinterpret_cast<const uint4*>(wstage + rr * kCodeRowBytes +
+                                                              ((k16 ^ (rr & 3)) * 16));
+                    if (m >= M) v = make_uint4(0, 0, 0, 0);
+                    if constexpr (EPI == kEpiQ8) {
+                        *reinterpret_cast<uint4*>(nx.xq + tiled_slot_offset<8>(m, n, N)) = v;
+                    } else {
+                        // split-nibble words: byte i = code i (low), code i + 4 (high)
+                        uint2 w;
+                        w.x = (v.x & 0x0F0F0F0Fu) | ((v.y & 0x0F0F0F0Fu) << 4);
+                        w.y = (v.z & 0x0F0F0F0Fu) | ((v.w & 0x0F0F0F0Fu) << 4);
+                        *reinterpret_cast<uint2*>(nx.xq + tiled_slot_offset<4>(m, n, N)) = w;
+                    }
+                }
+            }
+        }
+        return;
     }
     // 2. whole-line stores of this wave's rows (its own LDS writes are
     //    ordered before these reads)
@@ -803,24 +919,28 @@ hipError_t launch_skinny(const uint8_t* xq, const float* row_scale, const uint8_
     return hipGetLastError();
 }
 
-template <int FMT, int NS, bool ACC_OUT>
+template <int FMT, int NS, bool ACC_OUT, int EPI = kEpiBf16>
 hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                           const uint8_t* Wq, const float* w_scale, const float* comp_a,
                           const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
-                          int32_t* acc_out, hipStream_t stream) {
+                          int32_t* acc_out, hipStream_t stream,
+                          const NextLayerQuant& nx = NextLayerQuant{}) {
     using C = Cfg<FMT, NS>;
-    static_assert(C::lds_bytes(1) <= kLdsLimit, "LDS budget");
+    constexpr int kExtra = EPI != kEpiBf16 ? 1 : 0;
+    static_assert(C::lds_bytes(1, kExtra) <= kLdsLimit, "LDS budget");
+    static_assert(EPI == kEpiBf16 || Waves<FMT>::FW == 2, "code epilogue: 64 channels per wave");
     // the attribute admits the full CU; a call whose tables do not fit the
     // per-workgroup share simply runs fewer workgroups per CU
     static const hipError_t attr = hipFuncSetAttribute(
-        (const void*)w4_gemm_kernel<FMT, NS, ACC_OUT>,
+        (const void*)w4_gemm_kernel<FMT, NS, ACC_OUT, EPI>,
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
-    hipLaunchKernelGGL((w4_gemm_kernel<FMT, NS, ACC_OUT>), dim3((unsigned)(tiles_m * tiles_n)),
-                       dim3(kThreads), C::lds_bytes(S), stream, xq, row_scale, sid, Wq, w_scale,
-                       comp_a, comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n);
+    hipLaunchKernelGGL((w4_gemm_kernel<FMT, NS, ACC_OUT, EPI>),
+                       dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads),
+                       C::lds_bytes(S, kExtra), stream, xq, row_scale, sid, Wq, w_scale, comp_a,
+                       comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n, nx);
     return hipGetLastError();
 }
 
@@ -839,12 +959,14 @@ hipError_t launch_small(const uint8_t* xq, const float* row_scale, const uint8_t
 // Ring depth of the tiled kernel for S streams: the deepest (up to 4 stages)
 // that fits the per-workgroup LDS share with the call's tables.
 template <int FMT>
-int tiled_stages(int S) {
+int tiled_stages(int S, int extra_rows = 0) {
     // the two-stage ring fits every stream count
-    static_assert(Cfg<FMT, 2>::lds_bytes(RUDDER_MAX_STREAMS) <= 160 * 1024, "LDS budget");
-    if (Cfg<FMT, 4>::lds_bytes(1) <= kLdsLimit && Cfg<FMT, 4>::lds_bytes(S) <= kLdsLimit)
+    static_assert(Cfg<FMT, 2>::lds_bytes(RUDDER_MAX_STREAMS, 1) <= 160 * 1024, "LDS budget");
+    if (Cfg<FMT, 4>::lds_bytes(1, 1) <= kLdsLimit &&
+        Cfg<FMT, 4>::lds_bytes(S, extra_rows) <= kLdsLimit)
         return 4;
-    if (Cfg<FMT, 3>::lds_bytes(1) <= kLdsLimit && Cfg<FMT, 3>::lds_bytes(S) <= kLdsLimit)
+    if (Cfg<FMT, 3>::lds_bytes(1, 1) <= kLdsLimit &&
+        Cfg<FMT, 3>::lds_bytes(S, extra_rows) <= kLdsLimit)
         return 3;
     return 2;
 }
@@ -855,21 +977,24 @@ size_t tiled_lds_bytes(int ns, int S) {
                    : (ns == 3 ? Cfg<FMT, 3>::lds_bytes(S) : Cfg<FMT, 2>::lds_bytes(S));
 }
 
-template <int FMT, bool ACC_OUT>
+template <int FMT, bool ACC_OUT, int EPI = kEpiBf16>
 hipError_t launch_tiled(int ns, const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
-                        int32_t* acc_out, hipStream_t stream) {
-    if constexpr (Cfg<FMT, 4>::lds_bytes(1) <= kLdsLimit)
+                        int32_t* acc_out, hipStream_t stream,
+                        const NextLayerQuant& nx = NextLayerQuant{}) {
+    if constexpr (Cfg<FMT, 4>::lds_bytes(1, 1) <= kLdsLimit)
         if (ns == 4)
-            return launch_variant<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                   comp_b, M, N, K, S, Y, acc_out, stream);
-    if constexpr (Cfg<FMT, 3>::lds_bytes(1) <= kLdsLimit)
+            return launch_variant<FMT, 4, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                        comp_b, M, N, K, S, Y, acc_out, stream,
+                                                        nx);
+    if constexpr (Cfg<FMT, 3>::lds_bytes(1, 1) <= kLdsLimit)
         if (ns == 3)
-            return launch_variant<FMT, 3, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                   comp_b, M, N, K, S, Y, acc_out, stream);
-    return launch_variant<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
-                                           N, K, S, Y, acc_out, stream);
+            return launch_variant<FMT, 3, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                        comp_b, M, N, K, S, Y, acc_out, stream,
+                                                        nx);
+    return launch_variant<FMT, 2, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
+                                                M, N, K, S, Y, acc_out, stream, nx);
 }
 
 // Compute units of the current device (cached per device).
@@ -946,6 +1071,55 @@ hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* 
     if (abits == 8) RUDDER_LAUNCH(kFmtA8);
     RUDDER_LAUNCH(kFmtA4);
 #undef RUDDER_LAUNCH
+}
+
+namespace {
+
+template <int FMT>
+hipError_t launch_fused_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+                            const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                            const float* comp_b, int M, int N, int K, int S,
+                            const NextLayerQuant& nx, hipStream_t stream) {
+    const int ns = tiled_stages<FMT>(S, 1);
+    if (nx.codes == RUDDER_CODES_E2M3)
+        return launch_tiled<FMT, false, kEpiE2M3>(ns, xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                  comp_b, M, N, K, S, nullptr, nullptr, stream,
+                                                  nx);
+    if (nx.abits == 8)
+        return launch_tiled<FMT, false, kEpiQ8>(ns, xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                comp_b, M, N, K, S, nullptr, nullptr, stream, nx);
+    return launch_tiled<FMT, false, kEpiQ4>(ns, xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
+                                            M, N, K, S, nullptr, nullptr, stream, nx);
+}
+
+__global__ __launch_bounds__(256) void gelu_bf16_kernel(const uint16_t* __restrict__ in,
+                                                        uint16_t* __restrict__ out, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        out[i] = kGeluBf16[in[i]];
+}
+
+}  // namespace
+
+hipError_t launch_linear_gelu_quant(const void* Xq, const float* row_scale, const uint8_t* sid,
+                                    const uint8_t* Wq, const float* w_scale, const float* comp_a,
+                                    const float* comp_b, int M, int N, int K, int S, int abits,
+                                    int codes, const NextLayerQuant& next, hipStream_t stream) {
+    const uint8_t* xq = static_cast<const uint8_t*>(Xq);
+    if (codes == RUDDER_CODES_E2M3)
+        return launch_fused_fmt<kFmtF6>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
+                                        S, next, stream);
+    if (abits == 8)
+        return launch_fused_fmt<kFmtA8>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
+                                        S, next, stream);
+    return launch_fused_fmt<kFmtA4>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S,
+                                    next, stream);
+}
+
+hipError_t launch_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, hipStream_t stream) {
+    const size_t blocks = (n + 255) / 256;
+    hipLaunchKernelGGL(gelu_bf16_kernel, dim3((unsigned)(blocks < 65536 ? blocks : 65536)),
+                       dim3(256), 0, stream, in, out, n);
+    return hipGetLastError();
 }
 
 }  // namespace rudder

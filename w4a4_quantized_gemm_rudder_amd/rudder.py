@@ -5,10 +5,13 @@ behind the C ABI declared in include/rudder.h.  torch supplies device memory
 and the current HIP stream.  If the library is missing this module raises;
 there is no CPU fallback.
 
-The three calls keep their C names and meanings:
+The calls keep their C names and meanings:
   rudder_quantize_weights  -- offline weight preparation (SteerQuant Fig. 2, §4.2)
   rudder_quant_act         -- fused activation quantization (SteerQuant §4.3, §4.4)
   rudder_linear            -- low-bit GEMM + fused epilogue (SteerQuant §4.4)
+  rudder_linear_gelu_quant -- MLP up-projection with GELU (kept in BF16, App. D)
+                              and the down layer's quantizer in its epilogue
+  rudder_gelu_bf16         -- that GELU alone, elementwise
 (SteerQuant = "SteerQuant: Steering Quantization Error with Action-Guided
 Scaling in World-Action Models", paperlayer.ai digest.)
 """
@@ -33,6 +36,7 @@ MAX_STREAMS = 8
 EXPORTED = (
     "rudder_packed_weight_bytes", "rudder_packed_act_bytes", "rudder_quant_act_workspace_bytes",
     "rudder_quantize_weights", "rudder_quant_act", "rudder_linear",
+    "rudder_linear_gelu_quant", "rudder_gelu_bf16",
     "rudder_status_string", "rudder_last_error",
 )
 
@@ -68,6 +72,11 @@ def load_library() -> ctypes.CDLL:
     lib.rudder_quant_act.restype = i
     lib.rudder_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp]
     lib.rudder_linear.restype = i
+    lib.rudder_linear_gelu_quant.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
+                                             vp, vp, i, i, vp, vp, vp]
+    lib.rudder_linear_gelu_quant.restype = i
+    lib.rudder_gelu_bf16.argtypes = [vp, vp, sz, vp]
+    lib.rudder_gelu_bf16.restype = i
     lib.rudder_status_string.argtypes = [i]
     lib.rudder_status_string.restype = ctypes.c_char_p
     lib.rudder_last_error.argtypes = []
@@ -148,6 +157,20 @@ def rudder_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b,
         _ptr(comp_b), M, N, K, S, abits, codes, _ptr(Y), _ptr(acc_out), _stream(stream)))
 
 
+def rudder_linear_gelu_quant(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b,
+                             M: int, N: int, K: int, S: int, abits: int, codes: int,
+                             next_inv_smooth, next_act_scale, next_abits: int, next_codes: int,
+                             next_Xq, next_row_scale, stream=None) -> None:
+    _check(load_library().rudder_linear_gelu_quant(
+        _ptr(Xq), _ptr(row_scale), _ptr(stream_id), _ptr(Wq), _ptr(w_scale), _ptr(comp_a),
+        _ptr(comp_b), M, N, K, S, abits, codes, _ptr(next_inv_smooth), _ptr(next_act_scale),
+        next_abits, next_codes, _ptr(next_Xq), _ptr(next_row_scale), _stream(stream)))
+
+
+def rudder_gelu_bf16(x, out, n: int, stream=None) -> None:
+    _check(load_library().rudder_gelu_bf16(_ptr(x), _ptr(out), n, _stream(stream)))
+
+
 # ---------------------------------------------------------------------------
 # Allocating conveniences (torch allocates; the library computes)
 # ---------------------------------------------------------------------------
@@ -192,3 +215,28 @@ def linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b, M: int, N: int
     rudder_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b, M, N, K, S, abits,
                   codes, Y, acc, stream)
     return (Y, acc) if acc_out else Y
+
+
+def linear_gelu_quant(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b, M: int, N: int,
+                      K: int, S: int, abits: int, next_inv_smooth, next_act_scale,
+                      next_abits: int, codes: int = CODES_INT, next_codes: int = CODES_INT,
+                      stream=None):
+    """Returns (next Xq uint8, next row_scale fp32 [M]): the down layer's
+    packed input and row scales, from the up-projection's codes."""
+    import torch
+    dev = Wq.device
+    nxq = torch.empty(max(packed_act_bytes(M, N, next_abits, next_codes), 1), dtype=torch.uint8,
+                      device=dev)
+    nrs = torch.empty(max(M, 1), dtype=torch.float32, device=dev)
+    rudder_linear_gelu_quant(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b, M, N, K, S,
+                             abits, codes, next_inv_smooth, next_act_scale, next_abits,
+                             next_codes, nxq, nrs, stream)
+    return nxq, nrs
+
+
+def gelu_bf16(x, stream=None):
+    """GELU of a bf16 tensor (same table as the fused epilogue)."""
+    import torch
+    out = torch.empty_like(x)
+    rudder_gelu_bf16(x, out, x.numel(), stream)
+    return out

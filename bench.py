@@ -18,7 +18,10 @@ summed over the four linears, per second, both kernels of each linear
 included); `us_per_step` is the latency of one step.  `roofline` describes
 the kernel that takes the most time per step, timed live with HIP events
 around each of its launches on the launch stream.  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step.  `small_m` reports
+CPU oracle on a bounded sample of the same step.  `mlp_chained` times the
+same step with the MLP chained as in a DiT block (the down layer's input is
+GELU, kept in BF16, of the up-projection's output): unfused (bf16 output,
+GELU kernel, quantizer) and fused (rudder_linear_gelu_quant).  `small_m` reports
 action/proprio-sized calls (96 and 192 rows against full-width weights) as
 achieved HBM GB/s, timed as graph replays.
 
@@ -156,6 +159,70 @@ def run_step(t: int, wl, sid_d, layers, rudder, ev=None):
                              S, abits, codes, Ly["Y"], None)
         if ev is not None:
             ev[i][1].record()
+
+
+def run_chained_step(t: int, wl, sid_d, layers, rudder, fused: bool, gelu_buf):
+    """One step with the MLP chained as in a DiT block: the down layer's input
+    is GELU(up-projection output).  Unfused: up writes bf16, rudder_gelu_bf16,
+    rudder_quant_act for the down layer.  Fused: rudder_linear_gelu_quant
+    writes the down layer's codes and row scales from the up GEMM's epilogue.
+    The attention projections run as in run_step."""
+    S, M = wl.S, wl.M
+    tt = t % wl.n_steps
+    by_name = {Ly["name"]: Ly for Ly in layers}
+    up, down = by_name["up"], by_name["down"]
+
+    def comp(Ly):
+        ca = Ly["comp_a"][tt] if Ly["comp_a"].dim() == 3 else Ly["comp_a"]
+        cb = Ly["comp_b"][tt] if Ly["comp_b"].dim() == 3 else Ly["comp_b"]
+        return ca, cb
+
+    for Ly in layers:
+        if Ly["name"] == "down":
+            continue
+        K, N, abits, codes = Ly["K"], Ly["N"], Ly["abits"], Ly["codes"]
+        rudder.rudder_quant_act(Ly["X"], sid_d, Ly["inv"], Ly["delta"][tt], None, None, M, K, S,
+                                abits, codes, Ly["Xq"], Ly["rs"])
+        ca, cb = comp(Ly)
+        if Ly is up and fused:
+            rudder.rudder_linear_gelu_quant(up["Xq"], up["rs"], sid_d, up["Wq"], up["w_scale"], ca,
+                                            cb, M, N, K, S, abits, codes, down["inv"],
+                                            down["delta"][tt], down["abits"], down["codes"],
+                                            down["Xq"], down["rs"])
+        else:
+            rudder.rudder_linear(Ly["Xq"], Ly["rs"], sid_d, Ly["Wq"], Ly["w_scale"], ca, cb, M, N,
+                                 K, S, abits, codes, Ly["Y"], None)
+    if not fused:
+        rudder.rudder_gelu_bf16(up["Y"], gelu_buf, gelu_buf.numel())
+        rudder.rudder_quant_act(gelu_buf, sid_d, down["inv"], down["delta"][tt], None, None, M,
+                                down["K"], S, down["abits"], down["codes"], down["Xq"],
+                                down["rs"])
+    ca, cb = comp(down)
+    rudder.rudder_linear(down["Xq"], down["rs"], sid_d, down["Wq"], down["w_scale"], ca, cb, M,
+                         down["N"], down["K"], S, down["abits"], down["codes"], down["Y"], None)
+
+
+def time_chained(wl, sid_d, layers, rudder, torch, steps: int, warmup: int):
+    """µs per step of the chained-MLP step, unfused and fused."""
+    names = {Ly["name"] for Ly in layers}
+    if not {"up", "down"} <= names or any(Ly["delta"] is None for Ly in layers):
+        return None
+    up = next(Ly for Ly in layers if Ly["name"] == "up")
+    gelu_buf = torch.empty_like(up["Y"])
+    out = {}
+    for label, fused in (("unfused_gelu_quant", False), ("fused_gelu_quant", True)):
+        for t in range(warmup):
+            run_chained_step(t, wl, sid_d, layers, rudder, fused, gelu_buf)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for t in range(steps):
+            run_chained_step(t, wl, sid_d, layers, rudder, fused, gelu_buf)
+        e1.record()
+        torch.cuda.synchronize()
+        out[label + "_us_per_step"] = round(e0.elapsed_time(e1) / steps * 1e3, 1)
+    return out
 
 
 def gemm_kernel_tag(Ly, rudder) -> str:
@@ -460,6 +527,9 @@ def main():
         i8_us = int8_library_comparator(wl, layers, torch)
         if i8_us is not None:
             out["int8_library_gemm_us_per_step"] = round(i8_us, 1)
+    chained = time_chained(wl, sid_d, layers, rudder, torch, args.steps, args.warmup)
+    if chained is not None:
+        out["mlp_chained"] = chained
     if not args.no_small_m:
         out["small_m"] = small_m_calls(torch, rudder, args.w4a4_codes)
     if not args.no_cpu_baseline:

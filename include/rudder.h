@@ -249,6 +249,38 @@ rudder_status_t rudder_linear_gelu_quant(const void* Xq, const float* row_scale,
  */
 rudder_status_t rudder_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, void* stream);
 
+/*
+ * Calibration support (SteerQuant §4.2, §4.3, App. C: the shared diagonal and
+ * the layer-step thresholds and stream gains are chosen offline by a
+ * map-weighted reconstruction error whose weights differ per stream).
+ * For each stream s < S:  sse[s] = sum over rows m with stream_id[m] = s and
+ * all n of (float(Y[m][n]) - Yref[m][n])^2, accumulated in fp64 in a fixed
+ * order (deterministic).
+ *
+ *   Y          bf16 bits [M][N] (e.g. rudder_linear's output)
+ *   Yref       fp32 [M][N], the target
+ *   stream_id  uint8 [M], each < S
+ *   workspace  rudder_stream_sq_error_workspace_bytes() bytes of device scratch
+ *   sse        out: fp64 [S] (device)
+ *   M >= 0 (M = 0 writes sse = 0), N > 0, 1 <= S <= 8
+ * Errors: INVALID_ARG for a null pointer, M < 0, N <= 0, S outside 1..8.
+ */
+/*
+ * Calibration support (SteerQuant App. C.1: the activation-error target uses
+ * unquantized activations and the fixed quantized weights).  Unpacks Wq
+ * (either container) into out[k][n] = fl32(qw[k][n] * w_scale[n]), fp32
+ * [K][N] row-major.  K, N as for rudder_quantize_weights.
+ * Errors: INVALID_ARG for a null pointer, K or N <= 0 or not a multiple of 32
+ * (K of 64 for E2M3), an unknown container.
+ */
+rudder_status_t rudder_dequant_weights(const uint8_t* Wq, const float* w_scale, int K, int N,
+                                       int codes, float* out, void* stream);
+
+size_t rudder_stream_sq_error_workspace_bytes(void);
+rudder_status_t rudder_stream_sq_error(const uint16_t* Y, const float* Yref,
+                                       const uint8_t* stream_id, int M, int N, int S,
+                                       void* workspace, double* sse, void* stream);
+
 /* Static string naming a status code. */
 const char* rudder_status_string(rudder_status_t status);
 

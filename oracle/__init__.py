@@ -7,3 +7,4 @@ citations and the readings taken where the pages are silent.
 """
 from .oracle import *  # noqa: F401,F403
 from .oracle import __all__  # noqa: F401
+from . import calibration  # noqa: F401

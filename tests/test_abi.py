@@ -224,6 +224,18 @@ def test_gelu_bf16_validation(lib):
     assert lib.rudder_gelu_bf16(P, None, 10, None) == 1
 
 
+def test_calibration_support_validation(lib):
+    assert lib.rudder_dequant_weights(None, P, 64, 64, 0, P, None) == 1
+    assert lib.rudder_dequant_weights(P, P, 48, 64, 0, P, None) == 1
+    assert lib.rudder_dequant_weights(P, P, 96, 64, 1, P, None) == 1        # E2M3 needs K % 64
+    assert lib.rudder_dequant_weights(P, P, 64, 64, 3, P, None) == 1
+    assert lib.rudder_stream_sq_error_workspace_bytes() >= 8 * 8
+    assert lib.rudder_stream_sq_error(None, P, P, 4, 4, 1, P, P, None) == 1
+    assert lib.rudder_stream_sq_error(P, P, P, -1, 4, 1, P, P, None) == 1
+    assert lib.rudder_stream_sq_error(P, P, P, 4, 0, 1, P, P, None) == 1
+    assert lib.rudder_stream_sq_error(P, P, P, 4, 4, 9, P, P, None) == 1
+
+
 def test_misaligned_rejected(lib):
     assert _linear(lib, Y=P + 8) == 1
     assert _linear(lib, Wq=P + 4) == 1

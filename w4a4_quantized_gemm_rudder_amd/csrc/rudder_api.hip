@@ -222,6 +222,42 @@ rudder_status_t rudder_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, vo
     return from_hip(rudder::launch_gelu_bf16(in, out, n, static_cast<hipStream_t>(stream)), f);
 }
 
+rudder_status_t rudder_dequant_weights(const uint8_t* Wq, const float* w_scale, int K, int N,
+                                       int codes, float* out, void* stream) {
+    const char* f = "rudder_dequant_weights";
+    if (!Wq || !w_scale || !out) return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (K <= 0 || N <= 0 || K % 32 || N % 32)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d and N=%d must be positive multiples of 32",
+                    f, K, N);
+    if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
+    if (codes == RUDDER_CODES_E2M3 && K % 64)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 64 for E2M3 codes", f,
+                    K);
+    return from_hip(rudder::launch_dequant_weights(Wq, w_scale, K, N, codes, out,
+                                                   static_cast<hipStream_t>(stream)),
+                    f);
+}
+
+size_t rudder_stream_sq_error_workspace_bytes(void) {
+    return rudder::stream_sq_error_workspace_bytes();
+}
+
+rudder_status_t rudder_stream_sq_error(const uint16_t* Y, const float* Yref,
+                                       const uint8_t* stream_id, int M, int N, int S,
+                                       void* workspace, double* sse, void* stream) {
+    const char* f = "rudder_stream_sq_error";
+    if (!Y || !Yref || !stream_id || !workspace || !sse)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (M < 0 || N <= 0)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: M=%d must be >= 0 and N=%d > 0", f, M, N);
+    if (S < 1 || S > RUDDER_MAX_STREAMS)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: S=%d must be in 1..%d", f, S, RUDDER_MAX_STREAMS);
+    return from_hip(rudder::launch_stream_sq_error(Y, Yref, stream_id, M, N, S, workspace, sse,
+                                                   static_cast<hipStream_t>(stream)),
+                    f);
+}
+
 const char* rudder_status_string(rudder_status_t status) {
     switch (status) {
         case RUDDER_OK: return "RUDDER_OK";

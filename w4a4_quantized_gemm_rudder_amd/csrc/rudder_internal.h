@@ -50,6 +50,12 @@ hipError_t launch_linear_gelu_quant(const void* Xq, const float* row_scale, cons
 
 hipError_t launch_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, hipStream_t stream);
 
+hipError_t launch_dequant_weights(const uint8_t* Wq, const float* w_scale, int K, int N,
+                                  int codes, float* out, hipStream_t stream);
+size_t stream_sq_error_workspace_bytes();
+hipError_t launch_stream_sq_error(const uint16_t* Y, const float* Yref, const uint8_t* sid, int M,
+                                  int N, int S, void* workspace, double* sse, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // Device helpers
 // ---------------------------------------------------------------------------

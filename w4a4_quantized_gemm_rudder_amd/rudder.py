@@ -37,6 +37,7 @@ EXPORTED = (
     "rudder_packed_weight_bytes", "rudder_packed_act_bytes", "rudder_quant_act_workspace_bytes",
     "rudder_quantize_weights", "rudder_quant_act", "rudder_linear",
     "rudder_linear_gelu_quant", "rudder_gelu_bf16",
+    "rudder_dequant_weights", "rudder_stream_sq_error_workspace_bytes", "rudder_stream_sq_error",
     "rudder_status_string", "rudder_last_error",
 )
 
@@ -77,6 +78,12 @@ def load_library() -> ctypes.CDLL:
     lib.rudder_linear_gelu_quant.restype = i
     lib.rudder_gelu_bf16.argtypes = [vp, vp, sz, vp]
     lib.rudder_gelu_bf16.restype = i
+    lib.rudder_dequant_weights.argtypes = [vp, vp, i, i, i, vp, vp]
+    lib.rudder_dequant_weights.restype = i
+    lib.rudder_stream_sq_error_workspace_bytes.argtypes = []
+    lib.rudder_stream_sq_error_workspace_bytes.restype = sz
+    lib.rudder_stream_sq_error.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
+    lib.rudder_stream_sq_error.restype = i
     lib.rudder_status_string.argtypes = [i]
     lib.rudder_status_string.restype = ctypes.c_char_p
     lib.rudder_last_error.argtypes = []
@@ -169,6 +176,21 @@ def rudder_linear_gelu_quant(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp
 
 def rudder_gelu_bf16(x, out, n: int, stream=None) -> None:
     _check(load_library().rudder_gelu_bf16(_ptr(x), _ptr(out), n, _stream(stream)))
+
+
+def rudder_dequant_weights(Wq, w_scale, K: int, N: int, codes: int, out, stream=None) -> None:
+    _check(load_library().rudder_dequant_weights(_ptr(Wq), _ptr(w_scale), K, N, codes, _ptr(out),
+                                                 _stream(stream)))
+
+
+def stream_sq_error_workspace_bytes() -> int:
+    return int(load_library().rudder_stream_sq_error_workspace_bytes())
+
+
+def rudder_stream_sq_error(Y, Yref, stream_id, M: int, N: int, S: int, workspace, sse,
+                           stream=None) -> None:
+    _check(load_library().rudder_stream_sq_error(_ptr(Y), _ptr(Yref), _ptr(stream_id), M, N, S,
+                                                 _ptr(workspace), _ptr(sse), _stream(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -41,7 +41,7 @@ STREAM_NAMES = ("video", "proprio", "action")
 # Tensor tags used to derive independent RNG streams.
 _TAGS = {
     "x": 1, "x2": 2, "w": 3, "rho": 4, "gamma": 5, "a": 6, "b": 7,
-    "outlier_idx": 8, "z": 9,
+    "outlier_idx": 8, "z": 9, "calib": 10,
 }
 
 
@@ -296,3 +296,53 @@ def make_inputs(name: str, seed: int = 0, rows: Optional[int] = None,
         a, b = draw_compensation(shape, rng_for(seed, wi, "a", li), rng_for(seed, wi, "b", li))
         out.append(LayerInputs(layer, x, w, s, delta, a, b))
     return WorkloadInputs(wl, sid, out)
+
+
+# --------------------------------------------------------------------------
+# Calibration batches (offline search of the diagonal and the layer-step
+# table).  The action-impact map needs a trained model, so the map scores are
+# a fixed synthetic schedule with the qualitative shape the pages report
+# (proprioception leads at early steps, action at later ones [SteerQuant
+# §B.3]); the streams' activation statistics drift with the step.
+# --------------------------------------------------------------------------
+
+CALIB_SCORES = np.array([
+    # video, proprio, action
+    [0.30, 1.00, 0.55],
+    [0.35, 0.80, 0.75],
+    [0.40, 0.55, 0.95],
+    [0.40, 0.35, 1.00],
+])
+
+
+@dataclasses.dataclass
+class CalibrationInputs:
+    xs: List[np.ndarray]          # per step: bf16 bits [rows, K]
+    sids: List[np.ndarray]        # per step: uint8 [rows]
+    w: np.ndarray                 # bf16 bits [K, N]
+    scores: np.ndarray            # [steps, 3]
+
+
+def make_calibration(K: int, N: int, seed: int = 0, steps: int = 4,
+                     rows: Tuple[int, int, int] = (192, 16, 48),
+                     n_outliers: int = 0, outlier_factor: float = 20.0) -> CalibrationInputs:
+    """Per-step calibration batches of one layer: `rows` rows per stream
+    (video, proprio, action) at every step, video ~ N(0,1) with optional
+    outlier channels, proprio ~ N(0, (1.3 - 0.2 t)^2), action ~
+    N(0, (1.5 + 0.25 t)^2); W ~ N(0, 0.02)."""
+    rng_idx = rng_for(seed, 100, "outlier_idx", K)
+    out_idx = rng_idx.choice(K, size=n_outliers, replace=False) if n_outliers else None
+    xs, sids = [], []
+    for t in range(steps):
+        rng = rng_for(seed, 100, "calib", K, N, t)
+        parts, tags = [], []
+        for st, (n, sig) in enumerate(zip(rows, (1.0, 1.3 - 0.2 * t, 1.5 + 0.25 * t))):
+            x = rng.standard_normal((n, K)) * sig
+            if out_idx is not None and st == 0:
+                x[:, out_idx] *= outlier_factor
+            parts.append(x)
+            tags.append(np.full(n, st, np.uint8))
+        xs.append(to_bf16_bits(np.concatenate(parts)))
+        sids.append(np.concatenate(tags))
+    w = draw_w(K, N, 0.02, rng_for(seed, 100, "w", K, N))
+    return CalibrationInputs(xs=xs, sids=sids, w=w, scores=CALIB_SCORES[:steps].copy())

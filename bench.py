@@ -23,7 +23,8 @@ same step with the MLP chained as in a DiT block (the down layer's input is
 GELU, kept in BF16, of the up-projection's output): unfused (bf16 output,
 GELU kernel, quantizer) and fused (rudder_linear_gelu_quant).  `small_m` reports
 action/proprio-sized calls (96 and 192 rows against full-width weights) as
-achieved HBM GB/s, timed as graph replays.
+achieved HBM GB/s, timed as graph replays.  `calibration` times the offline
+search of one layer's diagonal and layer-step table with the GPU in the loop.
 
 --workload picks another workload (each printed as one JSON line of the
 same form, steps cycling through its step-indexed scale sets).
@@ -80,6 +81,10 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-small-m", action="store_true",
                    help="skip the few-row (weight-streaming) calls")
+    p.add_argument("--no-chained", action="store_true",
+                   help="skip the chained-MLP (unfused / fused GELU + quantize) timing")
+    p.add_argument("--no-calibration", action="store_true",
+                   help="skip the offline-calibration timing")
     p.add_argument("--no-bf16", action="store_true",
                    help="skip the library comparators (bf16 matmul, int8 GEMM)")
     p.add_argument("--cpu-rows", type=int, default=8384,
@@ -405,6 +410,26 @@ def small_m_calls(torch, rudder, w4a4_codes: str, reps: int = 20):
     return out
 
 
+def calibration_run(torch, W):
+    """Offline calibration of one hidden-2048 QKV layer (2048 -> 6144, W4A8)
+    from 4 steps x 256 calibration rows, GPU in the loop: wall time of the
+    whole search (both stages) and the number of quantize+GEMM passes."""
+    from w4a4_quantized_gemm_rudder_amd import calibrate as GC
+    ci = W.make_calibration(2048, 6144, seed=0, steps=4, rows=(192, 16, 48), n_outliers=20,
+                            outlier_factor=30.0)
+    weights = GC.map_weights(ci.scores)
+    GC.calibrate(ci.xs[:1], ci.sids[:1], ci.w, weights, 3, 8, alphas=(0.5,), rhos=(1.0,),
+                 gains=(1.0,))                                     # warm-up
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    res = GC.calibrate(ci.xs, ci.sids, ci.w, weights, 3, 8)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    return {"layer": "qkv 2048->6144 W4A8", "rows_per_step": 256, "steps": 4,
+            "passes": res.passes, "ms": round(dt * 1e3, 1),
+            "alpha": res.alpha, "rho_index": res.rho_index}
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -527,11 +552,14 @@ def main():
         i8_us = int8_library_comparator(wl, layers, torch)
         if i8_us is not None:
             out["int8_library_gemm_us_per_step"] = round(i8_us, 1)
-    chained = time_chained(wl, sid_d, layers, rudder, torch, args.steps, args.warmup)
+    chained = (None if args.no_chained else
+               time_chained(wl, sid_d, layers, rudder, torch, args.steps, args.warmup))
     if chained is not None:
         out["mlp_chained"] = chained
     if not args.no_small_m:
         out["small_m"] = small_m_calls(torch, rudder, args.w4a4_codes)
+    if not args.no_calibration:
+        out["calibration"] = calibration_run(torch, W)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.cpu_steps, args.seed)
     print(json.dumps(out), flush=True)

@@ -40,6 +40,24 @@ def test_gelu_every_bf16_pattern():
     assert_bits_equal("gelu", out.cpu().numpy().view(np.uint16), oracle.gelu_bf16(allb))
 
 
+@pytest.mark.parametrize("offset,n", [(1, 1001), (0, 13), (3, 70000)])
+def test_gelu_unaligned_and_tail(offset, n):
+    """The element-by-element path (unaligned buffers) and the tail after
+    the 8-wide groups."""
+    import torch
+    from w4a4_quantized_gemm_rudder_amd import rudder
+    log(f"case gelu offset={offset} n={n}")
+    rng = np.random.default_rng(n)
+    vals = rng.integers(0, 65536, n + offset).astype(np.uint16)
+    x = torch.from_numpy(vals.view(np.int16).copy()).cuda()
+    out = torch.zeros(n + offset, dtype=torch.int16, device="cuda")
+    rudder.rudder_gelu_bf16(x[offset:], out[offset:], n)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().view(np.uint16)
+    assert_bits_equal("gelu", got[offset:], oracle.gelu_bf16(vals[offset:]))
+    assert np.all(got[:offset] == 0)
+
+
 def run_fused(X, sid, Wb, s, a, b, delta, ninv, ndelta, S, abits, codes, nabits, ncodes,
               label=""):
     """Run rudder_linear_gelu_quant on the GPU and the oracle's composition;

@@ -19,6 +19,21 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxPartials = 1024;          // dynamic-mode partial-absmax blocks
 
+// 16 consecutive floats at a wave-uniform, 16-byte-aligned address, held in
+// scalar registers: marking each value wave-uniform keeps the loads scalar
+// even when lanes later select between two such groups.
+__device__ __forceinline__ void uniform_load16(const float* p, float (&o)[16]) {
+    const float4* q = reinterpret_cast<const float4*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const float4 v = q[j];
+        o[4 * j] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v.x)));
+        o[4 * j + 1] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v.y)));
+        o[4 * j + 2] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v.z)));
+        o[4 * j + 3] = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v.w)));
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Weight preparation: one block per 32 output channels.
 // ---------------------------------------------------------------------------
@@ -110,7 +125,10 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
     const int lane = tid & 63;
     const int kblocks = K >> 5;
     const int total = ((M + 31) >> 5) * kblocks;
-    const int gw = blockIdx.x * (kThreads / 64) + (tid >> 6);
+    // the block coordinates are wave-uniform (scalar registers), so the 32
+    // inverse smoothing factors of the block come through scalar loads and
+    // each lane selects its half
+    const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(tid >> 6);
     if (gw >= total) return;
     const int rb = gw / kblocks;
     const int kb = gw - rb * kblocks;
@@ -125,10 +143,12 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
         const uint4* xp = reinterpret_cast<const uint4*>(X + (size_t)r * K + k0);
         const uint4 x0 = xp[0], x1 = xp[1];
         const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        const float4* sp = reinterpret_cast<const float4*>(inv_smooth + k0);
-        const float4 s0 = sp[0], s1 = sp[1], s2 = sp[2], s3 = sp[3];
-        const float is[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                              s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+        float lo[16], hi[16], is[16];
+        uniform_load16(inv_smooth + kb * 32, lo);
+        uniform_load16(inv_smooth + kb * 32 + 16, hi);
+        const bool upper = lane >= 32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) is[i] = upper ? hi[i] : lo[i];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             const uint32_t h = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
@@ -179,7 +199,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
     const int lane = tid & 63;
     const int kblocks = K >> 6;
     const int total = ((M + 31) >> 5) * kblocks;
-    const int gw = blockIdx.x * (kThreads / 64) + (tid >> 6);
+    const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(tid >> 6);
     if (gw >= total) return;
     const int rb = gw / kblocks;
     const int kb = gw - rb * kblocks;
@@ -191,15 +211,19 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
         const int s = sid[r] & (RUDDER_MAX_STREAMS - 1);
         const float ia = s_ia[s];
         const uint4* xp = reinterpret_cast<const uint4*>(X + (size_t)r * K + k0);
-        const float4* sp = reinterpret_cast<const float4*>(inv_smooth + k0);
+        // wave-uniform block: its 64 inverse smoothing factors through scalar
+        // loads, each lane selecting its half
+        const float* sb = inv_smooth + kb * 64;
+        const bool upper = lane >= 32;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const uint4 x0 = xp[2 * h], x1 = xp[2 * h + 1];
             const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-            const float4 s0 = sp[4 * h], s1 = sp[4 * h + 1], s2 = sp[4 * h + 2],
-                         s3 = sp[4 * h + 3];
-            const float is[16] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w,
-                                  s2.x, s2.y, s2.z, s2.w, s3.x, s3.y, s3.z, s3.w};
+            float lo[16], hi[16], is[16];
+            uniform_load16(sb + 16 * h, lo);
+            uniform_load16(sb + 32 + 16 * h, hi);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) is[i] = upper ? hi[i] : lo[i];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const uint32_t hbits = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);

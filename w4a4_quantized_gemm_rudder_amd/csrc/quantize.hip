@@ -79,12 +79,12 @@ __global__ __launch_bounds__(kThreads) void quantize_weights_kernel(
         const int nn = blockIdx.x * 32 + jj;
         const int k0 = kSlot * (q >> 5);
         const float iw = s_inv_w[jj];
-        int c[kSlot];
+        float c[kSlot];
 #pragma unroll
         for (int i = 0; i < kSlot; ++i) {
             const int k = k0 + i;
             float w = bf16_bits_to_float(W[(size_t)k * N + nn]) * smooth[k];
-            c[i] = quantize_clamped(w * iw, 7.0f);
+            c[i] = quantize_clamped_f(w * iw, 7.0f);
         }
         if constexpr (CODES == RUDDER_CODES_E2M3) {
             uint32_t d[6];
@@ -94,9 +94,12 @@ __global__ __launch_bounds__(kThreads) void quantize_weights_kernel(
             *reinterpret_cast<uint4*>(blk + slot * 16) = make_uint4(d[0], d[1], d[2], d[3]);
             *reinterpret_cast<uint2*>(blk + 1024 + slot * 8) = make_uint2(d[4], d[5]);
         } else {
+            int ci[kSlot];
+#pragma unroll
+            for (int i = 0; i < kSlot; ++i) ci[i] = (int)c[i];
             uint2 out;
-            out.x = split_nibble_word(c);
-            out.y = split_nibble_word(c + 8);
+            out.x = split_nibble_word(ci);
+            out.y = split_nibble_word(ci + 8);
             *reinterpret_cast<uint2*>(Wq + tiled_slot_offset<4>(nn, k0, K)) = out;
         }
     }
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
     const int r = rb * 32 + (lane & 31);
     const int k0 = kb * 64 + 32 * (lane >> 5);
 
-    int c[32];
+    float c[32];
     if (r < M) {
         const int s = sid[r] & (RUDDER_MAX_STREAMS - 1);
         const float ia = s_ia[s];
@@ -228,13 +231,13 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
             for (int i = 0; i < 16; ++i) {
                 const uint32_t hbits = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
                 const float u = bf16_bits_to_float(hbits) * is[i];
-                c[16 * h + i] = quantize_clamped(u * ia, 7.0f);
+                c[16 * h + i] = quantize_clamped_f(u * ia, 7.0f);
             }
         }
         if (kb == 0 && lane < 32) row_scale[r] = s_delta[s];
     } else {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) c[i] = 0;
+        for (int i = 0; i < 32; ++i) c[i] = 0.0f;
     }
     uint32_t d[6];
     pack_e2m3x32(c, d);

@@ -111,27 +111,32 @@ __device__ __forceinline__ size_t tiled_slot_offset(int r, int k, int K) {
     return block * BLOCK_BYTES + (size_t)slot * SLOT_BYTES;
 }
 
-// FP6 E2M3 encoding of an integer code c in [-7, 7] (6 bits: sign in bit 5,
-// exponent bias 1 in bits 4..3, mantissa in bits 2..0).
-__device__ __forceinline__ uint32_t e2m3_code(int c) {
-    const uint32_t a = (uint32_t)(c < 0 ? -c : c);
-    // |c| = 0..7 -> 0x00 0x08 0x10 0x14 0x18 0x1A 0x1C 0x1E
-    const uint64_t table = 0x1E1C1A1814100800ull;
-    return (uint32_t)((table >> (8 * a)) & 0x3Fu) | (c < 0 ? 0x20u : 0u);
+// Symmetric quantizer to an integer-valued float: clamp to [-q, q], round
+// half to even, -0 folded to +0 (so a zero code always encodes as 0).
+__device__ __forceinline__ float quantize_clamped_f(float v, float q) {
+    v = fminf(fmaxf(v, -q), q);
+    return __builtin_rintf(v) + 0.0f;
 }
 
-// Pack 32 codes (t = 0..31) as a 192-bit little-endian string of 6-bit
-// E2M3 fields (field t at bits 6t..6t+5) into six dwords.
-__device__ __forceinline__ void pack_e2m3x32(const int* c, uint32_t (&d)[6]) {
+// Pack 32 integer-valued floats c_t in [-7, 7] (zero as +0) into the 192-bit
+// little-endian string of 6-bit FP6 E2M3 fields, field t at bits 6t..6t+5,
+// held in six dwords.  Each such value is exact in E2M3 (sign in bit 5,
+// exponent bias 1 in bits 4..3, mantissa in bits 2..0), so the gfx950
+// pack-convert with unit scale encodes it without rounding; that instruction
+// fills alternating fields from its two 16-wide operands (even t from the
+// first, odd t from the second).
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x6_t __attribute__((ext_vector_type(6)));
+__device__ __forceinline__ void pack_e2m3x32(const float* c, uint32_t (&d)[6]) {
+    f32x16_t even, odd;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) d[i] = 0;
-#pragma unroll
-    for (int t = 0; t < 32; ++t) {
-        const uint32_t v = e2m3_code(c[t]);
-        const int bit = 6 * t;
-        d[bit >> 5] |= v << (bit & 31);
-        if ((bit & 31) > 26) d[(bit >> 5) + 1] |= v >> (32 - (bit & 31));
+    for (int i = 0; i < 16; ++i) {
+        even[i] = c[2 * i];
+        odd[i] = c[2 * i + 1];
     }
+    const u32x6_t r = __builtin_amdgcn_cvt_scalef32_2xpk16_fp6_f32(even, odd, 1.0f);
+#pragma unroll
+    for (int i = 0; i < 6; ++i) d[i] = r[i];
 }
 
 // Byte offsets of slot (row r, k) in an E2M3 code matrix with K columns:

@@ -619,10 +619,10 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                 const uint4 hi = *reinterpret_cast<const uint4*>(
                     wstage + rr * kCodeRowBytes + (((2 * half + 1) ^ (rr & 3)) * 16));
                 const uint32_t w[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-                int c[32];
+                float c[32];
 #pragma unroll
                 for (int t = 0; t < 32; ++t)
-                    c[t] = m < M ? (int)(int8_t)((w[t >> 2] >> (8 * (t & 3))) & 0xFFu) : 0;
+                    c[t] = m < M ? (float)(int8_t)((w[t >> 2] >> (8 * (t & 3))) & 0xFFu) : 0.0f;
                 uint32_t d[6];
                 pack_e2m3x32(c, d);
                 uint8_t* blk = nx.xq + e2m3_block_offset(m, n0w, N);

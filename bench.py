@@ -85,6 +85,8 @@ def parse_args():
                    help="skip the chained-MLP (unfused / fused GELU + quantize) timing")
     p.add_argument("--no-calibration", action="store_true",
                    help="skip the offline-calibration timing")
+    p.add_argument("--no-ceiling", action="store_true",
+                   help="skip the MFMA-only ceiling on this workload's codes")
     p.add_argument("--no-bf16", action="store_true",
                    help="skip the library comparators (bf16 matmul, int8 GEMM)")
     p.add_argument("--cpu-rows", type=int, default=8384,
@@ -235,6 +237,42 @@ def gemm_kernel_tag(Ly, rudder) -> str:
     if Ly["codes"] == rudder.CODES_E2M3:
         return f"w4a{Ly['abits']}_e2m3_gemm"
     return f"w4a{Ly['abits']}_gemm"
+
+
+def mfma_ceiling(layers, rudder, torch, iters: int = 4000, reps: int = 5):
+    """MFMA-only rate of each GEMM kernel's matrix-core instruction on
+    fragments of that layer's own packed codes (as left by the timed steps),
+    and on all-zero codes.  The chip's clock falls with operand bit activity,
+    so the first figure is the attainable MFMA rate for this data; the
+    GEMM's own rate is set against it in `frac_of_ceiling`."""
+    sink = torch.empty(rudder.mfma_ceiling_sink_bytes() // 4, dtype=torch.int32, device="cuda")
+    out = {}
+    for Ly in layers:
+        tag = gemm_kernel_tag(Ly, rudder)
+        if tag in out:
+            continue
+        K, N, abits, codes = Ly["K"], Ly["N"], Ly["abits"], Ly["codes"]
+        M = Ly["rs"].numel()
+        ops = rudder.mfma_ceiling_ops(iters, codes)
+        res = {}
+        for name, Xq, Wq in (("workload_codes_tops", Ly["Xq"], Ly["Wq"]),
+                             ("zero_codes_tops", torch.zeros_like(Ly["Xq"]),
+                              torch.zeros_like(Ly["Wq"]))):
+            run = lambda: rudder.rudder_mfma_ceiling(Xq, Wq, M, N, K, abits, codes, iters, sink)
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            res[name] = round(ops * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        res["layer"] = f"{Ly['name']} {K}->{N}"
+        out[tag] = res
+    return out
 
 
 def load_traffic(kernel_tag: str, src_hash: str):
@@ -545,6 +583,14 @@ def main():
         "gemm_kernels": per_kernel,
         "wall_s": round(wall, 3),
     }
+    if not args.no_ceiling:
+        ceil = mfma_ceiling(layers, rudder, torch)
+        out["mfma_ceiling"] = ceil
+        for k, v in out["gemm_kernels"].items():
+            v["frac_of_ceiling"] = round(v["tops"] / ceil[k]["workload_codes_tops"], 4)
+        out["roofline"]["mfma_ceiling_tops"] = ceil[dominant]["workload_codes_tops"]
+        out["roofline"]["frac_of_ceiling"] = round(
+            achieved / ceil[dominant]["workload_codes_tops"], 4)
     if not args.no_bf16:
         bf16_us = bf16_comparator(wl, layers, torch)
         out["bf16_matmul_us_per_step"] = round(bf16_us, 1)

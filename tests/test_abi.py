@@ -1,7 +1,8 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads, exports
-every function include/rudder.h declares, sizes its buffers as documented,
-and rejects invalid arguments before touching the GPU."""
+every function the headers under include/ declare, sizes its buffers as
+documented, and rejects invalid arguments before touching the GPU."""
 import ctypes
+import glob
 import os
 import re
 
@@ -21,9 +22,11 @@ def lib():
 
 
 def header_functions():
-    text = open(os.path.join(ROOT, "include", "rudder.h")).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(rudder_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in sorted(glob.glob(os.path.join(ROOT, "include", "*.h"))):
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(rudder_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
@@ -240,3 +243,23 @@ def test_misaligned_rejected(lib):
     assert _linear(lib, Y=P + 8) == 1
     assert _linear(lib, Wq=P + 4) == 1
     assert _quant_act(lib, X=P + 2) == 1
+
+
+def test_mfma_ceiling_validation(lib):
+    from w4a4_quantized_gemm_rudder_amd import rudder as r
+    assert r.mfma_ceiling_sink_bytes() == 512 * 256 * 4
+    # 512 workgroups x 4 waves x iters x 16 MFMAs x ops per MFMA
+    assert r.mfma_ceiling_ops(10, r.CODES_INT) == 512 * 4 * 10 * 16 * 65536
+    assert r.mfma_ceiling_ops(10, r.CODES_E2M3) == 512 * 4 * 10 * 16 * 131072
+    assert r.mfma_ceiling_ops(0, r.CODES_INT) == 0
+
+    def call(**kw):
+        a = dict(Xq=P, Wq=P, M=64, N=64, K=128, abits=8, codes=0, iters=10, sink=P)
+        a.update(kw)
+        return lib.rudder_mfma_ceiling(a["Xq"], a["Wq"], a["M"], a["N"], a["K"], a["abits"],
+                                       a["codes"], a["iters"], a["sink"], None)
+    for kw in (dict(Xq=None), dict(Wq=None), dict(sink=None), dict(sink=P + 4), dict(M=0),
+               dict(N=48), dict(K=48), dict(abits=6), dict(codes=2), dict(codes=1, abits=8),
+               dict(codes=1, abits=4, K=96), dict(iters=0), dict(iters=(1 << 24) + 1)):
+        assert call(**kw) == 1, kw
+        assert len(lib.rudder_last_error()) > 0

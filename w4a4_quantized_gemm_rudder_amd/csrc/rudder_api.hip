@@ -258,6 +258,37 @@ rudder_status_t rudder_stream_sq_error(const uint16_t* Y, const float* Yref,
                     f);
 }
 
+size_t rudder_mfma_ceiling_sink_bytes(void) { return rudder::mfma_ceiling_sink_bytes(); }
+
+double rudder_mfma_ceiling_ops(int iters, int codes) {
+    return iters > 0 ? rudder::mfma_ceiling_ops(iters, codes) : 0.0;
+}
+
+rudder_status_t rudder_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K,
+                                    int abits, int codes, int iters, int32_t* sink,
+                                    void* stream) {
+    const char* f = "rudder_mfma_ceiling";
+    if (!Xq || !Wq || !sink) return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (misaligned(Xq) || misaligned(Wq) || misaligned(sink))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: Xq, Wq and sink must be 16-byte aligned", f);
+    if (abits != 4 && abits != 8)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
+    if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
+    if (codes == RUDDER_CODES_E2M3 && abits != 4)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: E2M3 codes need abits=4", f);
+    const int kmul = codes == RUDDER_CODES_E2M3 ? 64 : 32;
+    if (M <= 0 || N <= 0 || K <= 0 || N % 32 || K % kmul)
+        return fail(RUDDER_ERR_INVALID_ARG,
+                    "%s: M=%d, N=%d, K=%d: need M > 0, N a multiple of 32, K a multiple of %d", f,
+                    M, N, K, kmul);
+    if (iters <= 0 || iters > (1 << 24))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: iters=%d must be in 1..2^24", f, iters);
+    return from_hip(rudder::launch_mfma_ceiling(Xq, Wq, M, N, K, abits, codes, iters, sink,
+                                                static_cast<hipStream_t>(stream)),
+                    f);
+}
+
 const char* rudder_status_string(rudder_status_t status) {
     switch (status) {
         case RUDDER_OK: return "RUDDER_OK";

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "rudder.h"
+#include "rudder_diag.h"
 
 namespace rudder {
 
@@ -55,6 +56,13 @@ hipError_t launch_dequant_weights(const uint8_t* Wq, const float* w_scale, int K
 size_t stream_sq_error_workspace_bytes();
 hipError_t launch_stream_sq_error(const uint16_t* Y, const float* Yref, const uint8_t* sid, int M,
                                   int N, int S, void* workspace, double* sse, hipStream_t stream);
+
+// Matrix-core ceiling measurement (include/rudder_diag.h).
+size_t mfma_ceiling_sink_bytes();
+double mfma_ceiling_ops(int iters, int codes);
+hipError_t launch_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K,
+                               int abits, int codes, int iters, int32_t* sink,
+                               hipStream_t stream);
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -74,11 +74,16 @@ constexpr int kFmtA8 = 0;        // int8 activations, int4 weights (int8 MFMA)
 constexpr int kFmtA4 = 1;        // int4 activations and weights (int8 MFMA)
 constexpr int kFmtF6 = 2;        // 4-bit codes held as E2M3 (f8f6f4 MFMA)
 
-// Six dwords of one E2M3 fragment (plane 0: 16 bytes, plane 1: 8 bytes).
-struct F6Frag {
-    uint4 p0;
-    uint2 p1;
-};
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v6i __attribute__((ext_vector_type(6)));
+
+// The f8f6f4 scaled MFMA with 6-dword operands, as the instruction takes them
+// for FP6 formats (the clang builtin fixes 8-dword operands, which would make
+// every fragment a padded 8-register tuple and cost register moves).  Called
+// with cbsz = blgp = 2 (FP6 E2M3 A and B) and unit E8M0 scales only.
+__device__ v16f mfma_scale_f32_32x32x64_fp6(v6i a, v6i b, v16f c, int cbsz, int blgp,
+                                            int opsel_a, int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
 
 // Per-format traits.  The wave grid (kWavesN x kWavesM) splits the 128 x 256
 // block tile; each wave owns FW 32-channel and FA 32-token fragments, so
@@ -116,8 +121,8 @@ struct Fmt<kFmtF6> {
     static constexpr int kWBlock = 1536;
     static constexpr int kReadAhead = 1;
     static constexpr int kWavesN = 4;
-    typedef F6Frag WFrag;
-    typedef F6Frag AFrag;
+    typedef v6i WFrag;     // MFMA operand registers
+    typedef v6i AFrag;
     typedef v16f Acc;
 };
 
@@ -252,10 +257,20 @@ template <>
 __device__ __forceinline__ void read_frag<uint4>(const uint8_t* block, int lane, uint4& out) {
     out = *reinterpret_cast<const uint4*>(block + lane * 16);
 }
+// An E2M3 fragment, read straight into its 6-dword MFMA operand: plane 0
+// (16 bytes) into dwords 0..3 and plane 1 (8 bytes) into dwords 4..5.
 template <>
-__device__ __forceinline__ void read_frag<F6Frag>(const uint8_t* block, int lane, F6Frag& out) {
-    out.p0 = *reinterpret_cast<const uint4*>(block + lane * 16);
-    out.p1 = *reinterpret_cast<const uint2*>(block + 1024 + lane * 8);
+__device__ __forceinline__ void read_frag<v6i>(const uint8_t* block, int lane, v6i& out) {
+    const v4i p0 = *reinterpret_cast<const v4i*>(block + lane * 16);
+    // An opaque plane-1 address: otherwise the plane-1 reads of two fragments
+    // merge into one two-address read whose halves must then be moved into
+    // the two operand tuples.
+    uint32_t a1 = lds_offset(block + 1024 + lane * 8);
+    asm("" : "+v"(a1));
+    typedef __attribute__((address_space(3))) const v2i* lds_v2i_ptr;
+    const v2i p1 = *reinterpret_cast<lds_v2i_ptr>(static_cast<uintptr_t>(a1));
+    const v4i p1x = __builtin_shufflevector(p1, p1, 0, 1, -1, -1);
+    out = __builtin_shufflevector(p0, p1x, 0, 1, 2, 3, 4, 5);
 }
 
 template <int FMT, int NS>
@@ -272,32 +287,22 @@ __device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, int wn,
         read_frag(stage + (wm * FA + g) * C::kActPerMb + kk * C::kActBlock, lane, fr.a[g]);
 }
 
-// The 8-dword MFMA operand of an E2M3 fragment (the instruction reads the
-// first 6 dwords for FP6 operands).
-__device__ __forceinline__ v8i f6_operand(const F6Frag& f) {
-    return v8i{(int)f.p0.x, (int)f.p0.y, (int)f.p0.z, (int)f.p0.w, (int)f.p1.x, (int)f.p1.y,
-               0, 0};
-}
-
 // One k-substep: widen 4-bit fragments where needed and issue the FW x FA
-// MFMAs of the wave tile.
-template <int FMT>
+// MFMAs of the wave tile (E2M3: only those with index f * FA + g in
+// [FIRST, LAST), so the substep can be issued in two parts).
+template <int FMT, int FIRST = 0, int LAST = 1 << 20>
 __device__ __forceinline__ void mma_substep(
     const RawFrags<FMT>& fr, typename Fmt<FMT>::Acc (&acc)[Waves<FMT>::FW][Waves<FMT>::FA]) {
     constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
     if constexpr (FMT == kFmtF6) {
-        v8i wf[FW], af[FA];
-#pragma unroll
-        for (int f = 0; f < FW; ++f) wf[f] = f6_operand(fr.w[f]);
-#pragma unroll
-        for (int g = 0; g < FA; ++g) af[g] = f6_operand(fr.a[g]);
         // formats: 2 = FP6 E2M3 for both operands; scales 127 = 2^0 (E8M0)
 #pragma unroll
         for (int f = 0; f < FW; ++f)
 #pragma unroll
             for (int g = 0; g < FA; ++g)
-                acc[f][g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    wf[f], af[g], acc[f][g], 2, 2, 0, 127, 0, 127);
+                if (f * FA + g >= FIRST && f * FA + g < LAST)
+                    acc[f][g] = mfma_scale_f32_32x32x64_fp6(fr.w[f], fr.a[g], acc[f][g], 2, 2,
+                                                            0, 127, 0, 127);
     } else {
         v4i wf[FW], af[FA];
 #pragma unroll
@@ -486,6 +491,18 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                     const int ahead = kk + D;                // substep to read, relative to stage kt
                     const int rk = ahead % P;
                     const int rst = kt + ahead / P;          // its stage
+                    if constexpr (FMT == kFmtF6) {
+                        // E2M3: the substep's first MFMA goes ahead of the next
+                        // reads.  It waits for the substep's fragments, all
+                        // of which were read a substep earlier; the explicit
+                        // lgkmcnt(0) records that they have landed, so the
+                        // remaining MFMAs, issued after the next reads, carry
+                        // no wait on those reads (the compiler's own count is
+                        // conservative across the conditional barrier).
+                        mma_substep<FMT, 0, 1>(fr[j], acc);
+                        asm volatile("" : "+v"(acc[0][0]));
+                        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+                    }
                     if (rst < ksteps) {
                         if (ahead / P == 1 && rk == 0) {
                             // first read of stage kt+1: admit it, refill the ring
@@ -495,7 +512,17 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                         read_frags<FMT, NS>(lds + (rst % NS) * C::kStageBytes, rk, wn, wm, lane,
                                             fr[(j + D) % NSETS]);
                     }
-                    mma_substep<FMT>(fr[j], acc);
+                    if constexpr (FMT == kFmtF6) {
+                        mma_substep<FMT, 1>(fr[j], acc);
+                        // keep this substep's MFMAs ahead of the next
+                        // substep's reads (no sinking past the barrier)
+#pragma unroll
+                        for (int f = 0; f < FW; ++f)
+#pragma unroll
+                            for (int g = 0; g < FA; ++g) asm volatile("" : "+v"(acc[f][g]));
+                    } else {
+                        mma_substep<FMT>(fr[j], acc);
+                    }
                 }
             }
         }
@@ -695,20 +722,21 @@ constexpr int kSkinnyPitch = 33;                 // LDS row pitch (words) of the
 
 // Operand registers of one k-substep: the weight fragment and up to FA
 // activation fragments, already in MFMA operand form (E2M3 fragments are
-// loaded straight into 8-dword operands whose top two dwords stay zero).
+// loaded straight into 6-dword operands).
 template <int FMT, int FA>
 struct SkinnyOps {
-    typedef typename std::conditional<FMT == kFmtF6, v8i, uint2>::type WOp;
-    typedef typename std::conditional<FMT == kFmtF6, v8i,
+    typedef typename std::conditional<FMT == kFmtF6, v6i, uint2>::type WOp;
+    typedef typename std::conditional<FMT == kFmtF6, v6i,
             typename std::conditional<FMT == kFmtA8, uint4, uint2>::type>::type AOp;
     WOp w;
     AOp a[FA];
 };
 
-__device__ __forceinline__ v8i load_f6_operand(const uint8_t* block, int lane) {
-    const uint4 p0 = *reinterpret_cast<const uint4*>(block + lane * 16);
-    const uint2 p1 = *reinterpret_cast<const uint2*>(block + 1024 + lane * 8);
-    return v8i{(int)p0.x, (int)p0.y, (int)p0.z, (int)p0.w, (int)p1.x, (int)p1.y, 0, 0};
+__device__ __forceinline__ v6i load_f6_operand(const uint8_t* block, int lane) {
+    const v4i p0 = *reinterpret_cast<const v4i*>(block + lane * 16);
+    const v2i p1 = *reinterpret_cast<const v2i*>(block + 1024 + lane * 8);
+    return __builtin_shufflevector(p0, __builtin_shufflevector(p1, p1, 0, 1, -1, -1), 0, 1, 2,
+                                   3, 4, 5);
 }
 
 template <int FMT, int FA>
@@ -738,8 +766,7 @@ __device__ __forceinline__ void skinny_mma(const SkinnyOps<FMT, FA>& op, int mb,
 #pragma unroll
         for (int g = 0; g < FA; ++g)
             if (g < mb)
-                acc[g] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    op.w, op.a[g], acc[g], 2, 2, 0, 127, 0, 127);
+                acc[g] = mfma_scale_f32_32x32x64_fp6(op.w, op.a[g], acc[g], 2, 2, 0, 127, 0, 127);
     } else {
         const v4i wf = widen_nibbles(op.w.x, op.w.y);
 #pragma unroll

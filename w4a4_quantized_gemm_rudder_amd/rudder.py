@@ -39,6 +39,7 @@ EXPORTED = (
     "rudder_linear_gelu_quant", "rudder_gelu_bf16",
     "rudder_dequant_weights", "rudder_stream_sq_error_workspace_bytes", "rudder_stream_sq_error",
     "rudder_status_string", "rudder_last_error",
+    "rudder_mfma_ceiling_sink_bytes", "rudder_mfma_ceiling_ops", "rudder_mfma_ceiling",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -84,6 +85,12 @@ def load_library() -> ctypes.CDLL:
     lib.rudder_stream_sq_error_workspace_bytes.restype = sz
     lib.rudder_stream_sq_error.argtypes = [vp, vp, vp, i, i, i, vp, vp, vp]
     lib.rudder_stream_sq_error.restype = i
+    lib.rudder_mfma_ceiling_sink_bytes.argtypes = []
+    lib.rudder_mfma_ceiling_sink_bytes.restype = sz
+    lib.rudder_mfma_ceiling_ops.argtypes = [i, i]
+    lib.rudder_mfma_ceiling_ops.restype = ctypes.c_double
+    lib.rudder_mfma_ceiling.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp]
+    lib.rudder_mfma_ceiling.restype = i
     lib.rudder_status_string.argtypes = [i]
     lib.rudder_status_string.restype = ctypes.c_char_p
     lib.rudder_last_error.argtypes = []
@@ -262,3 +269,20 @@ def gelu_bf16(x, stream=None):
     out = torch.empty_like(x)
     rudder_gelu_bf16(x, out, x.numel(), stream)
     return out
+
+
+# ---------------------------------------------------------------------------
+# Measurement (include/rudder_diag.h)
+# ---------------------------------------------------------------------------
+def mfma_ceiling_sink_bytes() -> int:
+    return int(load_library().rudder_mfma_ceiling_sink_bytes())
+
+
+def mfma_ceiling_ops(iters: int, codes: int) -> float:
+    return float(load_library().rudder_mfma_ceiling_ops(iters, codes))
+
+
+def rudder_mfma_ceiling(Xq, Wq, M: int, N: int, K: int, abits: int, codes: int, iters: int,
+                        sink, stream=None) -> None:
+    _check(load_library().rudder_mfma_ceiling(_ptr(Xq), _ptr(Wq), M, N, K, abits, codes, iters,
+                                              _ptr(sink), _stream(stream)))

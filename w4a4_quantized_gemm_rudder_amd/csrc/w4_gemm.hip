@@ -29,7 +29,11 @@
 //     v_mfma_scale_f32_32x32x64_f8f6f4 directly (unit scales): no widening, and
 //     twice the int8 rate.  Products of codes are small integers and every
 //     fp32 partial sum is an integer below 2^24, so the fp32 accumulator holds
-//     the exact integer dot product.
+//     the exact integer dot product.  Its operands are the 6-dword form the
+//     instruction takes for FP6, read straight into place.  That loop is
+//     bound by LDS traffic, so each wave loads its own weight fragments (read
+//     by no other wave) from global memory into registers, two stages ahead;
+//     only the activations, shared by the four waves, go through the ring.
 //   * Tile order: workgroups are dealt round-robin to the 8 XCDs; the grid is
 //     remapped so each XCD walks a contiguous, m-grouped range of tiles and
 //     the tiles in flight on one XCD share activation and weight panels in
@@ -99,6 +103,7 @@ struct Fmt<kFmtA8> {
     static constexpr int kWBlock = 512;
     static constexpr int kReadAhead = 2;   // substeps of fragment read-ahead
     static constexpr int kWavesN = 4;      // waves along the channel dimension
+    static constexpr bool kDirectW = false; // weights staged through the LDS ring
     typedef uint2 WFrag;
     typedef uint4 AFrag;
     typedef v16i Acc;
@@ -110,6 +115,7 @@ struct Fmt<kFmtA4> {
     static constexpr int kWBlock = 512;
     static constexpr int kReadAhead = 2;
     static constexpr int kWavesN = 4;
+    static constexpr bool kDirectW = false;
     typedef uint2 WFrag;
     typedef uint2 AFrag;
     typedef v16i Acc;
@@ -121,6 +127,10 @@ struct Fmt<kFmtF6> {
     static constexpr int kWBlock = 1536;
     static constexpr int kReadAhead = 1;
     static constexpr int kWavesN = 4;
+    // Each wave is the only reader of its weight fragments (one wave per
+    // 64-channel slice), so they go straight from global memory into
+    // registers; only the activations, read by all four waves, use the ring.
+    static constexpr bool kDirectW = true;
     typedef v6i WFrag;     // MFMA operand registers
     typedef v6i AFrag;
     typedef v16f Acc;
@@ -143,7 +153,7 @@ struct Cfg {
     static constexpr int kActBytes = (BM / 32) * kActPerMb;
     static constexpr int kWBlock = F::kWBlock;
     static constexpr int kWPerNb = (BK / F::kKSub) * kWBlock;        // per 32-channel block
-    static constexpr int kWBytes = (BN / 32) * kWPerNb;
+    static constexpr int kWBytes = F::kDirectW ? 0 : (BN / 32) * kWPerNb;
     static constexpr int kStageBytes = kActBytes + kWBytes;
     static constexpr int kRingBytes = NS * kStageBytes;
     // 16-byte direct loads per thread per stage (each wave instruction = 1 KiB)
@@ -287,23 +297,14 @@ __device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, int wn,
         read_frag(stage + (wm * FA + g) * C::kActPerMb + kk * C::kActBlock, lane, fr.a[g]);
 }
 
-// One k-substep: widen 4-bit fragments where needed and issue the FW x FA
-// MFMAs of the wave tile (E2M3: only those with index f * FA + g in
-// [FIRST, LAST), so the substep can be issued in two parts).
-template <int FMT, int FIRST = 0, int LAST = 1 << 20>
+// One k-substep of the int formats: widen 4-bit fragments and issue the
+// FW x FA MFMAs of the wave tile.
+template <int FMT>
 __device__ __forceinline__ void mma_substep(
     const RawFrags<FMT>& fr, typename Fmt<FMT>::Acc (&acc)[Waves<FMT>::FW][Waves<FMT>::FA]) {
     constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
-    if constexpr (FMT == kFmtF6) {
-        // formats: 2 = FP6 E2M3 for both operands; scales 127 = 2^0 (E8M0)
-#pragma unroll
-        for (int f = 0; f < FW; ++f)
-#pragma unroll
-            for (int g = 0; g < FA; ++g)
-                if (f * FA + g >= FIRST && f * FA + g < LAST)
-                    acc[f][g] = mfma_scale_f32_32x32x64_fp6(fr.w[f], fr.a[g], acc[f][g], 2, 2,
-                                                            0, 127, 0, 127);
-    } else {
+    static_assert(FMT != kFmtF6, "E2M3 has its own loop");
+    {
         v4i wf[FW], af[FA];
 #pragma unroll
         for (int f = 0; f < FW; ++f) wf[f] = widen_nibbles(fr.w[f].x, fr.w[f].y);
@@ -424,8 +425,8 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         act_src[i] = Xq + (size_t)gmb * kblocks * C::kActBlock + rem;
         act_dst[i] = byte;
     }
-    const uint8_t* w_src[C::kWLoads];
-    int w_dst[C::kWLoads];
+    const uint8_t* w_src[C::kWLoads > 0 ? C::kWLoads : 1];
+    int w_dst[C::kWLoads > 0 ? C::kWLoads : 1];
 #pragma unroll
     for (int i = 0; i < C::kWLoads; ++i) {
         const int byte = (uwave * C::kWLoads + i) * 1024;
@@ -457,15 +458,12 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0;
 
     // ---- main loop ----------------------------------------------------------
+    if constexpr (!F::kDirectW) {
     // Prologue: fill all NS buffers, wait for stage 0.
     const int pre = min(NS, ksteps);
     for (int s = 0; s < pre; ++s) issue_stage(s);
     wait_stages_and_barrier<L>(pre - 1);
 
-    // Fragments are read one k-substep ahead of the MFMAs that use them.  The
-    // barrier that admits stage kt+1 sits after the reads of stage kt's last
-    // substep and before its MFMAs, so the MFMA pipe has work queued while
-    // the workgroup synchronizes and the next stage's first fragments load.
     // Fragments are read D k-substeps ahead of the MFMAs that use them
     // (global substep j = kt * P + kk uses register set fr[j % NSETS]).  The
     // barrier that admits stage kt+1 sits right before the first read of
@@ -491,18 +489,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                     const int ahead = kk + D;                // substep to read, relative to stage kt
                     const int rk = ahead % P;
                     const int rst = kt + ahead / P;          // its stage
-                    if constexpr (FMT == kFmtF6) {
-                        // E2M3: the substep's first MFMA goes ahead of the next
-                        // reads.  It waits for the substep's fragments, all
-                        // of which were read a substep earlier; the explicit
-                        // lgkmcnt(0) records that they have landed, so the
-                        // remaining MFMAs, issued after the next reads, carry
-                        // no wait on those reads (the compiler's own count is
-                        // conservative across the conditional barrier).
-                        mma_substep<FMT, 0, 1>(fr[j], acc);
-                        asm volatile("" : "+v"(acc[0][0]));
-                        __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
-                    }
                     if (rst < ksteps) {
                         if (ahead / P == 1 && rk == 0) {
                             // first read of stage kt+1: admit it, refill the ring
@@ -512,20 +498,117 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                         read_frags<FMT, NS>(lds + (rst % NS) * C::kStageBytes, rk, wn, wm, lane,
                                             fr[(j + D) % NSETS]);
                     }
-                    if constexpr (FMT == kFmtF6) {
-                        mma_substep<FMT, 1>(fr[j], acc);
-                        // keep this substep's MFMAs ahead of the next
-                        // substep's reads (no sinking past the barrier)
-#pragma unroll
-                        for (int f = 0; f < FW; ++f)
-#pragma unroll
-                            for (int g = 0; g < FA; ++g) asm volatile("" : "+v"(acc[f][g]));
-                    } else {
-                        mma_substep<FMT>(fr[j], acc);
-                    }
+                    mma_substep<FMT>(fr[j], acc);
                 }
             }
         }
+    }
+    } else {
+    // E2M3: activations through a two-stage LDS ring, weight fragments
+    // straight from global memory into two register sets, one per stage
+    // parity.  Stage kt's weights sit in wreg[kt % 2]; each substep's slot is
+    // refilled with stage kt+2's fragments as soon as that substep's MFMAs
+    // are issued, so a weight load has two stages to land.  Activation
+    // fragments are read one substep ahead (fa[kk] holds substep kk).
+    static_assert(NS == 2 && BK / F::kKSub == 2, "E2M3 loop bookkeeping");
+    constexpr int P = 2;                              // substeps per stage
+    constexpr int WL = 2 * FW;                        // weight loads per substep (p0 + p1)
+    // this wave's weight block rows (wave-uniform: scalar bases; every lane
+    // adds its own 16- and 8-byte offsets)
+    const uint8_t* wblk[FW];
+    const int uwn = uwave % kWavesN;
+#pragma unroll
+    for (int f = 0; f < FW; ++f) {
+        const int gnb = min(tile_n * (BN / 32) + uwn * FW + f, nblocks - 1);
+        wblk[f] = Wq + (size_t)gnb * kblocks * F::kWBlock;
+    }
+    const uint32_t off0 = lane * 16, off1 = 1024 + lane * 8;
+    auto load_w = [&](int kt, int kk, v6i (&dst)[FW]) {
+#pragma unroll
+        for (int f = 0; f < FW; ++f) {
+            const uint8_t* b = wblk[f] + (size_t)(kt * P + kk) * F::kWBlock;
+            const v4i p0 = *reinterpret_cast<const v4i*>(b + off0);
+            const v2i p1 = *reinterpret_cast<const v2i*>(b + off1);
+            dst[f] = __builtin_shufflevector(p0, __builtin_shufflevector(p1, p1, 0, 1, -1, -1),
+                                             0, 1, 2, 3, 4, 5);
+        }
+    };
+    auto read_acts = [&](int kt, int kk, v6i (&dst)[FA]) {
+        const uint8_t* st = lds + (kt % NS) * C::kStageBytes + kk * C::kActBlock;
+#pragma unroll
+        for (int g = 0; g < FA; ++g) read_frag(st + (wm * FA + g) * C::kActPerMb, lane, dst[g]);
+    };
+    auto mma = [&](const v6i (&w)[FW], const v6i (&a)[FA], int first, int last) {
+        // formats: 2 = FP6 E2M3 for both operands; scales 127 = 2^0 (E8M0)
+#pragma unroll
+        for (int f = 0; f < FW; ++f)
+#pragma unroll
+            for (int g = 0; g < FA; ++g)
+                if (f * FA + g >= first && f * FA + g < last)
+                    acc[f][g] = mfma_scale_f32_32x32x64_fp6(w[f], a[g], acc[f][g], 2, 2, 0, 127,
+                                                            0, 127);
+    };
+
+    // Prologue, in this order: ring stages 0 and 1, then the weights of
+    // stages 0 and 1.  vmcnt counts in issue order; a wait for a ring stage
+    // leaves outstanding only what was issued after it.  Weight loads are
+    // issued unconditionally (past the last stage they re-read the last
+    // stage's blocks into a slot that is not used again), which keeps the
+    // counts below fixed and the compiler's own waits for the weight
+    // registers exact.
+    v6i wreg[2][P][FW];
+    v6i fa[P][FA];
+    const int klast = ksteps - 1;
+    issue_stage(0);
+    if (ksteps > 1) issue_stage(1);
+    load_w(0, 0, wreg[0][0]);
+    load_w(0, 1, wreg[0][1]);
+    load_w(min(1, klast), 0, wreg[1][0]);
+    load_w(min(1, klast), 1, wreg[1][1]);
+    if (ksteps > 1) wait_and_barrier<C::kActLoads + 4 * WL>();
+    else wait_and_barrier<4 * WL>();
+    read_acts(0, 0, fa[0]);
+
+    // One stage; u = kt % 2 selects the weight register set.
+    auto stage = [&](int kt, auto u_) {
+        constexpr int u = decltype(u_)::value;
+#pragma unroll
+        for (int kk = 0; kk < P; ++kk) {
+            // The substep's first MFMA goes ahead of the next reads.  It
+            // waits for the substep's activation fragments, all read a
+            // substep earlier; the explicit lgkmcnt(0) records that they
+            // have landed, so the remaining MFMAs, issued after the next
+            // reads, carry no wait on those reads.
+            mma(wreg[u][kk], fa[kk], 0, 1);
+            asm volatile("" : "+v"(acc[0][0]));
+            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+            if (kk == 0) {
+                read_acts(kt, 1, fa[1]);
+            } else if (kt < klast) {
+                // Admit stage kt+1.  Its ring loads were issued at the
+                // previous boundary (in the prologue for kt = 0); after them
+                // came the weight loads of the substeps since then.
+                if (kt == 0) wait_and_barrier<5 * WL>();
+                else wait_and_barrier<2 * WL>();
+                if (kt + 2 < ksteps) issue_stage(kt + 2);
+                read_acts(kt + 1, 0, fa[0]);
+            }
+            mma(wreg[u][kk], fa[kk], 1, FW * FA);
+            // keep this substep's MFMAs ahead of what follows (no sinking
+            // past the barrier or the slot refill)
+#pragma unroll
+            for (int f = 0; f < FW; ++f)
+#pragma unroll
+                for (int g = 0; g < FA; ++g) asm volatile("" : "+v"(acc[f][g]));
+            load_w(min(kt + 2, klast), kk, wreg[u][kk]);
+        }
+    };
+    int kt = 0;
+    for (; kt + 1 < ksteps; kt += 2) {
+        stage(kt, std::integral_constant<int, 0>{});
+        stage(kt + 1, std::integral_constant<int, 1>{});
+    }
+    if (kt < ksteps) stage(kt, std::integral_constant<int, 0>{});
     }
 
     // ---- fused epilogue -------------------------------------------------
@@ -987,6 +1070,8 @@ hipError_t launch_small(const uint8_t* xq, const float* row_scale, const uint8_t
 // that fits the per-workgroup LDS share with the call's tables.
 template <int FMT>
 int tiled_stages(int S, int extra_rows = 0) {
+    // the E2M3 loop (weights in registers) keeps a two-stage activation ring
+    if constexpr (Fmt<FMT>::kDirectW) return 2;
     // the two-stage ring fits every stream count
     static_assert(Cfg<FMT, 2>::lds_bytes(RUDDER_MAX_STREAMS, 1) <= 160 * 1024, "LDS budget");
     if (Cfg<FMT, 4>::lds_bytes(1, 1) <= kLdsLimit &&
@@ -1010,12 +1095,12 @@ hipError_t launch_tiled(int ns, const uint8_t* xq, const float* row_scale, const
                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                         int32_t* acc_out, hipStream_t stream,
                         const NextLayerQuant& nx = NextLayerQuant{}) {
-    if constexpr (Cfg<FMT, 4>::lds_bytes(1, 1) <= kLdsLimit)
+    if constexpr (!Fmt<FMT>::kDirectW && Cfg<FMT, 4>::lds_bytes(1, 1) <= kLdsLimit)
         if (ns == 4)
             return launch_variant<FMT, 4, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
                                                         comp_b, M, N, K, S, Y, acc_out, stream,
                                                         nx);
-    if constexpr (Cfg<FMT, 3>::lds_bytes(1, 1) <= kLdsLimit)
+    if constexpr (!Fmt<FMT>::kDirectW && Cfg<FMT, 3>::lds_bytes(1, 1) <= kLdsLimit)
         if (ns == 3)
             return launch_variant<FMT, 3, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
                                                         comp_b, M, N, K, S, Y, acc_out, stream,

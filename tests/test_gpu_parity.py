@@ -117,6 +117,9 @@ SMALL_M = [
     (100, 4096, 12288, 3, 4, True, 26, CODES_E2M3),
     (128, 128, 96, 5, 4, False, 27, CODES_E2M3),
     (2, 256, 64, 2, 8, True, 28, CODES_INT),
+    # more than 128 rows on a narrow layer: 64-row groups fill more CUs
+    (192, 2048, 2048, 3, 4, False, 29, CODES_E2M3),
+    (250, 512, 1024, 3, 8, True, 30, CODES_INT),
 ]
 
 
@@ -135,6 +138,7 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     (8292, 128, 2048, 3, 8, False, 40, CODES_INT),
     (8292, 256, 2048, 3, 4, True, 41, CODES_E2M3),
     (8292, 128, 2048, 2, 4, False, 42, CODES_INT),
+    (8384, 256, 2048, 3, 4, False, 43, CODES_E2M3),     # 192-row remainder
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")

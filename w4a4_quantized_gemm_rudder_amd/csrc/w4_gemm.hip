@@ -1054,12 +1054,30 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
     return hipGetLastError();
 }
 
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n <= 0)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
 template <int FMT, bool ACC_OUT>
 hipError_t launch_small(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                         int32_t* acc_out, hipStream_t stream) {
-    if (M <= 64)
+    // 64-row groups for few rows, and when several 128-row groups would
+    // still leave compute units idle (the 192-row remainder of a 2048-wide
+    // layer: 128 workgroups of 128 rows, 192 of 64)
+    if (M <= 64 || (M > 128 && (N / 32) * ((M + 127) / 128) < device_cus()))
         return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
                                               M, N, K, S, Y, acc_out, stream);
     return launch_skinny<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
@@ -1109,20 +1127,6 @@ hipError_t launch_tiled(int ns, const uint8_t* xq, const float* row_scale, const
                                                 M, N, K, S, Y, acc_out, stream, nx);
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static int cus[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cus[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            n <= 0)
-            n = 256;
-        cus[dev] = n;
-    }
-    return cus[dev];
-}
 
 template <int FMT, bool ACC_OUT>
 hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* sid,

@@ -18,6 +18,18 @@
 #include "rudder_internal.h"
 
 namespace rudder {
+typedef int mfma_v6i __attribute__((ext_vector_type(6)));
+typedef float mfma_v16f __attribute__((ext_vector_type(16)));
+
+// The f8f6f4 scaled MFMA with the 6-dword operands it takes for FP6 formats
+// (the same instruction form as the GEMM's).
+__device__ mfma_v16f mfma_scale_f32_32x32x64_fp6(mfma_v6i a, mfma_v6i b, mfma_v16f c,
+                                                 int cbsz, int blgp, int opsel_a, int scale_a,
+                                                 int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
+}  // namespace rudder
+
+namespace rudder {
 namespace {
 
 typedef int v2i __attribute__((ext_vector_type(2)));
@@ -26,11 +38,6 @@ typedef int v6i __attribute__((ext_vector_type(6)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// The f8f6f4 scaled MFMA with the 6-dword operands it takes for FP6 formats
-// (the same instruction form as the GEMM's).
-__device__ v16f mfma_scale_f32_32x32x64_fp6(v6i a, v6i b, v16f c, int cbsz, int blgp,
-                                            int opsel_a, int scale_a, int opsel_b, int scale_b)
-    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
 
 constexpr int kThreads = 256;
 constexpr int kFW = 2, kFA = 4, kSets = 2;

@@ -16,12 +16,14 @@
 //     bytes equal to 16 * code in natural k order.  The int32 result is then
 //     16x (W4A8) or 256x (W4A4) the true accumulator -- exact for
 //     K <= RUDDER_MAX_K -- and an arithmetic shift undoes it.
-//   * Codes arrive MFMA-tiled (32 x 32 blocks in lane order), so global ->
-//     LDS traffic uses the gfx950 direct-to-LDS 16-byte loads (no VGPR
-//     staging, one contiguous KiB per wave instruction) into an NS-stage LDS
-//     ring, and every fragment read is a contiguous lane-ordered ds_read.
-//   * One workgroup barrier per k-stage: loads for stage kt+NS-1 are issued
-//     right after the barrier that retires stage kt-1's buffer.
+//   * Codes arrive MFMA-tiled (blocks in lane order), so every fragment is
+//     one contiguous lane-ordered load.  The activation fragments, shared by
+//     the workgroup's four waves, go global -> LDS with the gfx950
+//     direct-to-LDS 16-byte loads (no VGPR staging, one contiguous KiB per
+//     wave instruction) into a two-stage ring, one workgroup barrier per
+//     k-stage.  Each wave is the only reader of its weight fragments, so
+//     those go straight from global memory into registers, two stages ahead,
+//     and cost no LDS traffic.
 //   * Epilogue: dequantize + compensate in registers, stage the bf16 tile in
 //     LDS (XOR-swizzled 16-byte chunks), then store whole 512-byte row
 //     segments with 16-byte stores so every HBM line is written once.
@@ -30,10 +32,7 @@
 //     twice the int8 rate.  Products of codes are small integers and every
 //     fp32 partial sum is an integer below 2^24, so the fp32 accumulator holds
 //     the exact integer dot product.  Its operands are the 6-dword form the
-//     instruction takes for FP6, read straight into place.  That loop is
-//     bound by LDS traffic, so each wave loads its own weight fragments (read
-//     by no other wave) from global memory into registers, two stages ahead;
-//     only the activations, shared by the four waves, go through the ring.
+//     instruction takes for FP6, read straight into place.
 //   * Tile order: workgroups are dealt round-robin to the 8 XCDs; the grid is
 //     remapped so each XCD walks a contiguous, m-grouped range of tiles and
 //     the tiles in flight on one XCD share activation and weight panels in
@@ -41,6 +40,20 @@
 #include <type_traits>
 
 #include "rudder_internal.h"
+
+namespace rudder {
+typedef int mfma_v6i __attribute__((ext_vector_type(6)));
+typedef float mfma_v16f __attribute__((ext_vector_type(16)));
+
+// The f8f6f4 scaled MFMA with 6-dword operands, as the instruction takes them
+// for FP6 formats (the clang builtin fixes 8-dword operands, which would make
+// every fragment a padded 8-register tuple and cost register moves).  Called
+// with cbsz = blgp = 2 (FP6 E2M3 A and B) and unit E8M0 scales only.
+__device__ mfma_v16f mfma_scale_f32_32x32x64_fp6(mfma_v6i a, mfma_v6i b, mfma_v16f c,
+                                                 int cbsz, int blgp, int opsel_a, int scale_a,
+                                                 int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
+}  // namespace rudder
 
 namespace rudder {
 namespace {
@@ -81,19 +94,12 @@ constexpr int kFmtF6 = 2;        // 4-bit codes held as E2M3 (f8f6f4 MFMA)
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v6i __attribute__((ext_vector_type(6)));
 
-// The f8f6f4 scaled MFMA with 6-dword operands, as the instruction takes them
-// for FP6 formats (the clang builtin fixes 8-dword operands, which would make
-// every fragment a padded 8-register tuple and cost register moves).  Called
-// with cbsz = blgp = 2 (FP6 E2M3 A and B) and unit E8M0 scales only.
-__device__ v16f mfma_scale_f32_32x32x64_fp6(v6i a, v6i b, v16f c, int cbsz, int blgp,
-                                            int opsel_a, int scale_a, int opsel_b, int scale_b)
-    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v6i32.v6i32");
 
-// Per-format traits.  The wave grid (kWavesN x kWavesM) splits the 128 x 256
-// block tile; each wave owns FW 32-channel and FA 32-token fragments, so
-// every k-substep it reads FW weight and FA activation fragments from LDS and
-// issues FW * FA MFMAs.  (With int8 activations a 2 x 2 grid reads 20% fewer
-// LDS bytes per MFMA than 1 x 4, and measured no faster.)
+// Per-format traits.  The wave grid (kWavesN x kWavesM = 4 x 1) splits the
+// 128 x 256 block tile; each wave owns FW = 2 32-channel and FA = 4 32-token
+// fragments, so every k-substep it takes FW weight fragments (its own, from
+// registers) and FA activation fragments (shared, from LDS) and issues
+// FW * FA MFMAs.
 template <int FMT>
 struct Fmt;
 template <>
@@ -101,9 +107,7 @@ struct Fmt<kFmtA8> {
     static constexpr int kKSub = 32;       // k per MFMA
     static constexpr int kABlock = 1024;   // bytes per 32-row x kKSub code block
     static constexpr int kWBlock = 512;
-    static constexpr int kReadAhead = 2;   // substeps of fragment read-ahead
     static constexpr int kWavesN = 4;      // waves along the channel dimension
-    static constexpr bool kDirectW = false; // weights staged through the LDS ring
     typedef uint2 WFrag;
     typedef uint4 AFrag;
     typedef v16i Acc;
@@ -113,9 +117,7 @@ struct Fmt<kFmtA4> {
     static constexpr int kKSub = 32;
     static constexpr int kABlock = 512;
     static constexpr int kWBlock = 512;
-    static constexpr int kReadAhead = 2;
     static constexpr int kWavesN = 4;
-    static constexpr bool kDirectW = false;
     typedef uint2 WFrag;
     typedef uint2 AFrag;
     typedef v16i Acc;
@@ -125,12 +127,7 @@ struct Fmt<kFmtF6> {
     static constexpr int kKSub = 64;
     static constexpr int kABlock = 1536;
     static constexpr int kWBlock = 1536;
-    static constexpr int kReadAhead = 1;
     static constexpr int kWavesN = 4;
-    // Each wave is the only reader of its weight fragments (one wave per
-    // 64-channel slice), so they go straight from global memory into
-    // registers; only the activations, read by all four waves, use the ring.
-    static constexpr bool kDirectW = true;
     typedef v6i WFrag;     // MFMA operand registers
     typedef v6i AFrag;
     typedef v16f Acc;
@@ -151,15 +148,11 @@ struct Cfg {
     static constexpr int kActBlock = F::kABlock;
     static constexpr int kActPerMb = (BK / F::kKSub) * kActBlock;    // per 32-token block
     static constexpr int kActBytes = (BM / 32) * kActPerMb;
-    static constexpr int kWBlock = F::kWBlock;
-    static constexpr int kWPerNb = (BK / F::kKSub) * kWBlock;        // per 32-channel block
-    static constexpr int kWBytes = F::kDirectW ? 0 : (BN / 32) * kWPerNb;
-    static constexpr int kStageBytes = kActBytes + kWBytes;
+    // the ring holds activation codes only (weights go to registers)
+    static constexpr int kStageBytes = kActBytes;
     static constexpr int kRingBytes = NS * kStageBytes;
     // 16-byte direct loads per thread per stage (each wave instruction = 1 KiB)
     static constexpr int kActLoads = kActBytes / (1024 * kWaves);
-    static constexpr int kWLoads = kWBytes / (1024 * kWaves);
-    static constexpr int kLoads = kActLoads + kWLoads;
     static constexpr int kEpiBytes = BM * BN * 2;                    // bf16 tile
     // Per-tile epilogue tables (w_scale, comp_a[S], comp_b[S] for the tile's
     // 256 channels, 1 KiB each) live after both the ring and the bf16 tile.
@@ -219,16 +212,6 @@ __device__ __forceinline__ void wait_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" : : "n"(N) : "memory");
 }
 
-template <int L>
-__device__ __forceinline__ void wait_stages_and_barrier(int stages_in_flight) {
-    // stages_in_flight is 0..4
-    if (stages_in_flight >= 4) wait_and_barrier<4 * L>();
-    else if (stages_in_flight == 3) wait_and_barrier<3 * L>();
-    else if (stages_in_flight == 2) wait_and_barrier<2 * L>();
-    else if (stages_in_flight == 1) wait_and_barrier<L>();
-    else wait_and_barrier<0>();
-}
-
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
     return (uint32_t)(uintptr_t)(lds_ptr_t)p;
 }
@@ -249,13 +232,6 @@ __device__ __forceinline__ void tile_of_block(int bid, int nblk, int tiles_m, in
     tm = first_m + local % gm;
     tn = local / gm;
 }
-
-// Raw (still packed) fragment words of one k-substep.
-template <int FMT>
-struct RawFrags {
-    typename Fmt<FMT>::WFrag w[Waves<FMT>::FW];     // channel blocks
-    typename Fmt<FMT>::AFrag a[Waves<FMT>::FA];     // token blocks
-};
 
 template <typename T>
 __device__ __forceinline__ void read_frag(const uint8_t* block, int lane, T& out);
@@ -283,47 +259,6 @@ __device__ __forceinline__ void read_frag<v6i>(const uint8_t* block, int lane, v
     out = __builtin_shufflevector(p0, p1x, 0, 1, 2, 3, 4, 5);
 }
 
-template <int FMT, int NS>
-__device__ __forceinline__ void read_frags(const uint8_t* stage, int kk, int wn, int wm,
-                                           int lane, RawFrags<FMT>& fr) {
-    using C = Cfg<FMT, NS>;
-    constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
-    const uint8_t* wst = stage + C::kActBytes;
-#pragma unroll
-    for (int f = 0; f < FW; ++f)
-        read_frag(wst + (wn * FW + f) * C::kWPerNb + kk * C::kWBlock, lane, fr.w[f]);
-#pragma unroll
-    for (int g = 0; g < FA; ++g)
-        read_frag(stage + (wm * FA + g) * C::kActPerMb + kk * C::kActBlock, lane, fr.a[g]);
-}
-
-// One k-substep of the int formats: widen 4-bit fragments and issue the
-// FW x FA MFMAs of the wave tile.
-template <int FMT>
-__device__ __forceinline__ void mma_substep(
-    const RawFrags<FMT>& fr, typename Fmt<FMT>::Acc (&acc)[Waves<FMT>::FW][Waves<FMT>::FA]) {
-    constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
-    static_assert(FMT != kFmtF6, "E2M3 has its own loop");
-    {
-        v4i wf[FW], af[FA];
-#pragma unroll
-        for (int f = 0; f < FW; ++f) wf[f] = widen_nibbles(fr.w[f].x, fr.w[f].y);
-#pragma unroll
-        for (int g = 0; g < FA; ++g) {
-            if constexpr (FMT == kFmtA8)
-                af[g] = v4i{(int)fr.a[g].x, (int)fr.a[g].y, (int)fr.a[g].z, (int)fr.a[g].w};
-            else
-                af[g] = widen_nibbles(fr.a[g].x, fr.a[g].y);
-        }
-#pragma unroll
-        for (int f = 0; f < FW; ++f)
-#pragma unroll
-            for (int g = 0; g < FA; ++g)
-                acc[f][g] =
-                    __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[f], af[g], acc[f][g], 0, 0, 0);
-    }
-}
-
 // Exact integer value of an accumulator element (the int8 path carries 16x
 // (W4A8) or 256x (W4A4) the true sum, see widen_nibbles).
 template <int FMT>
@@ -342,7 +277,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, NextLayerQuant nx) {
     using C = Cfg<FMT, NS>;
     using F = Fmt<FMT>;
-    constexpr int L = C::kLoads;
     constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
     constexpr int kWavesN = Waves<FMT>::kN;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
@@ -408,11 +342,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     }
 
     // ---- per-wave direct-load sources ------------------------------------
-    // Each wave instruction moves one contiguous KiB: for activations the
-    // (32-token block, k-block) pairs of this stage, for weights the
-    // (32-channel block, k-block) pairs.  Bases are wave-uniform (SGPRs);
-    // every lane adds lane * 16.  Token / channel blocks past the matrix edge
-    // are clamped to the last real block (their results are never stored).
+    // Each wave instruction moves one contiguous KiB of the stage's
+    // activation codes (32-token block, k-block pairs).  Bases are
+    // wave-uniform (SGPRs); every lane adds lane * 16.  Token blocks past the
+    // matrix edge are clamped to the last real block (their results are never
+    // stored).
     const uint32_t voff = lane * 16;
     const uint8_t* act_src[C::kActLoads];
     int act_dst[C::kActLoads];
@@ -425,28 +359,13 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         act_src[i] = Xq + (size_t)gmb * kblocks * C::kActBlock + rem;
         act_dst[i] = byte;
     }
-    const uint8_t* w_src[C::kWLoads > 0 ? C::kWLoads : 1];
-    int w_dst[C::kWLoads > 0 ? C::kWLoads : 1];
-#pragma unroll
-    for (int i = 0; i < C::kWLoads; ++i) {
-        const int byte = (uwave * C::kWLoads + i) * 1024;
-        const int nb = byte / C::kWPerNb;
-        const int rem = byte - nb * C::kWPerNb;
-        const int gnb = min(tile_n * (BN / 32) + nb, nblocks - 1);
-        w_src[i] = Wq + (size_t)gnb * kblocks * C::kWBlock + rem;
-        w_dst[i] = C::kActBytes + byte;
-    }
 
     auto issue_stage = [&](int kt) {
         const uint32_t base = lds_base + (uint32_t)((kt % NS) * C::kStageBytes);
         const size_t a_off = (size_t)kt * C::kActPerMb;
-        const size_t w_off = (size_t)kt * C::kWPerNb;
 #pragma unroll
         for (int i = 0; i < C::kActLoads; ++i)
             load_lds16(act_src[i] + a_off, voff, base + act_dst[i]);
-#pragma unroll
-        for (int i = 0; i < C::kWLoads; ++i)
-            load_lds16(w_src[i] + w_off, voff, base + w_dst[i]);
     };
 
     typename F::Acc acc[FW][FA];
@@ -458,63 +377,22 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             for (int r = 0; r < 16; ++r) acc[f][g][r] = 0;
 
     // ---- main loop ----------------------------------------------------------
-    if constexpr (!F::kDirectW) {
-    // Prologue: fill all NS buffers, wait for stage 0.
-    const int pre = min(NS, ksteps);
-    for (int s = 0; s < pre; ++s) issue_stage(s);
-    wait_stages_and_barrier<L>(pre - 1);
-
-    // Fragments are read D k-substeps ahead of the MFMAs that use them
-    // (global substep j = kt * P + kk uses register set fr[j % NSETS]).  The
-    // barrier that admits stage kt+1 sits right before the first read of
-    // that stage, after every read of stage kt, so the MFMA pipe still has
-    // queued substeps while the workgroup synchronizes.
-    constexpr int P = BK / F::kKSub;                 // substeps per stage
-    constexpr int D = F::kReadAhead;                 // read-ahead distance
-    constexpr int NSETS = 2 * D;                     // register sets in rotation
-    constexpr int U = NSETS > P ? NSETS / P : 1;     // stages per unrolled iteration
-    static_assert((P * U) % NSETS == 0 && D <= P, "substep bookkeeping");
-    RawFrags<FMT> fr[NSETS];
-#pragma unroll
-    for (int j = 0; j < D; ++j)
-        read_frags<FMT, NS>(lds + (j / P) * C::kStageBytes, j % P, wn, wm, lane, fr[j]);
-    for (int kt0 = 0; kt0 < ksteps; kt0 += U) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int kt = kt0 + u;
-            if (kt < ksteps) {
-#pragma unroll
-                for (int kk = 0; kk < P; ++kk) {
-                    const int j = (u * P + kk) % NSETS;      // substep index mod NSETS
-                    const int ahead = kk + D;                // substep to read, relative to stage kt
-                    const int rk = ahead % P;
-                    const int rst = kt + ahead / P;          // its stage
-                    if (rst < ksteps) {
-                        if (ahead / P == 1 && rk == 0) {
-                            // first read of stage kt+1: admit it, refill the ring
-                            wait_stages_and_barrier<L>(min(NS - 2, ksteps - 2 - kt));
-                            if (kt + NS < ksteps) issue_stage(kt + NS);
-                        }
-                        read_frags<FMT, NS>(lds + (rst % NS) * C::kStageBytes, rk, wn, wm, lane,
-                                            fr[(j + D) % NSETS]);
-                    }
-                    mma_substep<FMT>(fr[j], acc);
-                }
-            }
-        }
-    }
-    } else {
-    // E2M3: activations through a two-stage LDS ring, weight fragments
-    // straight from global memory into two register sets, one per stage
-    // parity.  Stage kt's weights sit in wreg[kt % 2]; each substep's slot is
+    // Weights straight from global memory into registers, activations
+    // through a two-stage LDS ring.  Each wave is the only reader of its
+    // weight fragments (one wave per 64-channel slice), so those bypass LDS:
+    // stage kt's weights sit in wreg[kt % 2], and each substep's slot is
     // refilled with stage kt+2's fragments as soon as that substep's MFMAs
-    // are issued, so a weight load has two stages to land.  Activation
-    // fragments are read one substep ahead (fa[kk] holds substep kk).
-    static_assert(NS == 2 && BK / F::kKSub == 2, "E2M3 loop bookkeeping");
-    constexpr int P = 2;                              // substeps per stage
-    constexpr int WL = 2 * FW;                        // weight loads per substep (p0 + p1)
+    // are issued, which gives a weight load two stages to land.  Activation
+    // fragments are read one substep ahead into fa[j % 2] (substep j).
+    static_assert(NS == 2, "direct-weight loop bookkeeping");
+    constexpr int P = BK / F::kKSub;                  // substeps per stage
+    static_assert(P % 2 == 0, "substep parity");
+    constexpr bool kF6 = FMT == kFmtF6;
+    constexpr int WL = kF6 ? 2 * FW : FW;             // weight loads per substep
+    typedef typename F::WFrag WOp;
+    typedef typename F::AFrag AOp;
     // this wave's weight block rows (wave-uniform: scalar bases; every lane
-    // adds its own 16- and 8-byte offsets)
+    // adds its own offsets)
     const uint8_t* wblk[FW];
     const int uwn = uwave % kWavesN;
 #pragma unroll
@@ -522,31 +400,52 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         const int gnb = min(tile_n * (BN / 32) + uwn * FW + f, nblocks - 1);
         wblk[f] = Wq + (size_t)gnb * kblocks * F::kWBlock;
     }
-    const uint32_t off0 = lane * 16, off1 = 1024 + lane * 8;
-    auto load_w = [&](int kt, int kk, v6i (&dst)[FW]) {
+    const uint32_t off0 = lane * (kF6 ? 16 : 8), off1 = 1024 + lane * 8;
+    auto load_w = [&](int kt, int kk, WOp (&dst)[FW]) {
 #pragma unroll
         for (int f = 0; f < FW; ++f) {
             const uint8_t* b = wblk[f] + (size_t)(kt * P + kk) * F::kWBlock;
-            const v4i p0 = *reinterpret_cast<const v4i*>(b + off0);
-            const v2i p1 = *reinterpret_cast<const v2i*>(b + off1);
-            dst[f] = __builtin_shufflevector(p0, __builtin_shufflevector(p1, p1, 0, 1, -1, -1),
-                                             0, 1, 2, 3, 4, 5);
+            if constexpr (kF6) {
+                const v4i p0 = *reinterpret_cast<const v4i*>(b + off0);
+                const v2i p1 = *reinterpret_cast<const v2i*>(b + off1);
+                dst[f] = __builtin_shufflevector(
+                    p0, __builtin_shufflevector(p1, p1, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5);
+            } else {
+                dst[f] = *reinterpret_cast<const uint2*>(b + off0);
+            }
         }
     };
-    auto read_acts = [&](int kt, int kk, v6i (&dst)[FA]) {
+    auto read_acts = [&](int kt, int kk, AOp (&dst)[FA]) {
         const uint8_t* st = lds + (kt % NS) * C::kStageBytes + kk * C::kActBlock;
 #pragma unroll
         for (int g = 0; g < FA; ++g) read_frag(st + (wm * FA + g) * C::kActPerMb, lane, dst[g]);
     };
-    auto mma = [&](const v6i (&w)[FW], const v6i (&a)[FA], int first, int last) {
-        // formats: 2 = FP6 E2M3 for both operands; scales 127 = 2^0 (E8M0)
+    auto mma = [&](const WOp (&w)[FW], const AOp (&a)[FA], int first, int last) {
 #pragma unroll
-        for (int f = 0; f < FW; ++f)
+        for (int f = 0; f < FW; ++f) {
+            if constexpr (kF6) {
+                // formats: 2 = FP6 E2M3 for both operands; scales 127 = 2^0 (E8M0)
 #pragma unroll
-            for (int g = 0; g < FA; ++g)
-                if (f * FA + g >= first && f * FA + g < last)
-                    acc[f][g] = mfma_scale_f32_32x32x64_fp6(w[f], a[g], acc[f][g], 2, 2, 0, 127,
-                                                            0, 127);
+                for (int g = 0; g < FA; ++g)
+                    if (f * FA + g >= first && f * FA + g < last)
+                        acc[f][g] = mfma_scale_f32_32x32x64_fp6(w[f], a[g], acc[f][g], 2, 2, 0,
+                                                                127, 0, 127);
+            } else {
+                if (f * FA + FA <= first || f * FA >= last) continue;
+                const v4i wf = widen_nibbles(w[f].x, w[f].y);
+#pragma unroll
+                for (int g = 0; g < FA; ++g) {
+                    if (f * FA + g < first || f * FA + g >= last) continue;
+                    v4i af;
+                    if constexpr (FMT == kFmtA8)
+                        af = v4i{(int)a[g].x, (int)a[g].y, (int)a[g].z, (int)a[g].w};
+                    else
+                        af = widen_nibbles(a[g].x, a[g].y);
+                    acc[f][g] =
+                        __builtin_amdgcn_mfma_i32_32x32x32_i8(wf, af, acc[f][g], 0, 0, 0);
+                }
+            }
+        }
     };
 
     // Prologue, in this order: ring stages 0 and 1, then the weights of
@@ -556,17 +455,18 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     // stage's blocks into a slot that is not used again), which keeps the
     // counts below fixed and the compiler's own waits for the weight
     // registers exact.
-    v6i wreg[2][P][FW];
-    v6i fa[P][FA];
+    constexpr int LA = C::kActLoads;
+    WOp wreg[2][P][FW];
+    AOp fa[2][FA];
     const int klast = ksteps - 1;
     issue_stage(0);
     if (ksteps > 1) issue_stage(1);
-    load_w(0, 0, wreg[0][0]);
-    load_w(0, 1, wreg[0][1]);
-    load_w(min(1, klast), 0, wreg[1][0]);
-    load_w(min(1, klast), 1, wreg[1][1]);
-    if (ksteps > 1) wait_and_barrier<C::kActLoads + 4 * WL>();
-    else wait_and_barrier<4 * WL>();
+#pragma unroll
+    for (int kk = 0; kk < P; ++kk) load_w(0, kk, wreg[0][kk]);
+#pragma unroll
+    for (int kk = 0; kk < P; ++kk) load_w(min(1, klast), kk, wreg[1][kk]);
+    if (ksteps > 1) wait_and_barrier<LA + 2 * P * WL>();
+    else wait_and_barrier<2 * P * WL>();
     read_acts(0, 0, fa[0]);
 
     // One stage; u = kt % 2 selects the weight register set.
@@ -579,21 +479,21 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             // substep earlier; the explicit lgkmcnt(0) records that they
             // have landed, so the remaining MFMAs, issued after the next
             // reads, carry no wait on those reads.
-            mma(wreg[u][kk], fa[kk], 0, 1);
+            mma(wreg[u][kk], fa[kk % 2], 0, 1);
             asm volatile("" : "+v"(acc[0][0]));
             __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
-            if (kk == 0) {
-                read_acts(kt, 1, fa[1]);
+            if (kk + 1 < P) {
+                read_acts(kt, kk + 1, fa[(kk + 1) % 2]);
             } else if (kt < klast) {
                 // Admit stage kt+1.  Its ring loads were issued at the
                 // previous boundary (in the prologue for kt = 0); after them
-                // came the weight loads of the substeps since then.
-                if (kt == 0) wait_and_barrier<5 * WL>();
-                else wait_and_barrier<2 * WL>();
+                // came the weight refills of the substeps since then.
+                if (kt == 0) wait_and_barrier<(3 * P - 1) * WL>();
+                else wait_and_barrier<P * WL>();
                 if (kt + 2 < ksteps) issue_stage(kt + 2);
                 read_acts(kt + 1, 0, fa[0]);
             }
-            mma(wreg[u][kk], fa[kk], 1, FW * FA);
+            mma(wreg[u][kk], fa[kk % 2], 1, FW * FA);
             // keep this substep's MFMAs ahead of what follows (no sinking
             // past the barrier or the slot refill)
 #pragma unroll
@@ -609,7 +509,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         stage(kt + 1, std::integral_constant<int, 1>{});
     }
     if (kt < ksteps) stage(kt, std::integral_constant<int, 0>{});
-    }
 
     // ---- fused epilogue -------------------------------------------------
     // 1. registers: t = float(acc) * (row_scale * w_scale); y = fma(a, t, b);
@@ -1084,49 +983,21 @@ hipError_t launch_small(const uint8_t* xq, const float* row_scale, const uint8_t
                                           N, K, S, Y, acc_out, stream);
 }
 
-// Ring depth of the tiled kernel for S streams: the deepest (up to 4 stages)
-// that fits the per-workgroup LDS share with the call's tables.
-template <int FMT>
-int tiled_stages(int S, int extra_rows = 0) {
-    // the E2M3 loop (weights in registers) keeps a two-stage activation ring
-    if constexpr (Fmt<FMT>::kDirectW) return 2;
-    // the two-stage ring fits every stream count
-    static_assert(Cfg<FMT, 2>::lds_bytes(RUDDER_MAX_STREAMS, 1) <= 160 * 1024, "LDS budget");
-    if (Cfg<FMT, 4>::lds_bytes(1, 1) <= kLdsLimit &&
-        Cfg<FMT, 4>::lds_bytes(S, extra_rows) <= kLdsLimit)
-        return 4;
-    if (Cfg<FMT, 3>::lds_bytes(1, 1) <= kLdsLimit &&
-        Cfg<FMT, 3>::lds_bytes(S, extra_rows) <= kLdsLimit)
-        return 3;
-    return 2;
-}
-
-template <int FMT>
-size_t tiled_lds_bytes(int ns, int S) {
-    return ns == 4 ? Cfg<FMT, 4>::lds_bytes(S)
-                   : (ns == 3 ? Cfg<FMT, 3>::lds_bytes(S) : Cfg<FMT, 2>::lds_bytes(S));
-}
+// The tiled kernel's LDS ring holds two stages of activation codes.
+constexpr int kRing = 2;
 
 template <int FMT, bool ACC_OUT, int EPI = kEpiBf16>
-hipError_t launch_tiled(int ns, const uint8_t* xq, const float* row_scale, const uint8_t* sid,
+hipError_t launch_tiled(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                         int32_t* acc_out, hipStream_t stream,
                         const NextLayerQuant& nx = NextLayerQuant{}) {
-    if constexpr (!Fmt<FMT>::kDirectW && Cfg<FMT, 4>::lds_bytes(1, 1) <= kLdsLimit)
-        if (ns == 4)
-            return launch_variant<FMT, 4, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                        comp_b, M, N, K, S, Y, acc_out, stream,
-                                                        nx);
-    if constexpr (!Fmt<FMT>::kDirectW && Cfg<FMT, 3>::lds_bytes(1, 1) <= kLdsLimit)
-        if (ns == 3)
-            return launch_variant<FMT, 3, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                        comp_b, M, N, K, S, Y, acc_out, stream,
-                                                        nx);
-    return launch_variant<FMT, 2, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
-                                                M, N, K, S, Y, acc_out, stream, nx);
+    // every stream count fits a CU (calls with many streams may run one
+    // workgroup per CU instead of two)
+    static_assert(Cfg<FMT, kRing>::lds_bytes(RUDDER_MAX_STREAMS, 1) <= 160 * 1024, "LDS budget");
+    return launch_variant<FMT, kRing, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                    comp_b, M, N, K, S, Y, acc_out, stream, nx);
 }
-
 
 template <int FMT, bool ACC_OUT>
 hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
@@ -1137,7 +1008,6 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
     if (M <= kSkinnyMaxM)
         return launch_small<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N,
                                           K, S, Y, acc_out, stream);
-    const int ns = tiled_stages<FMT>(S);
     // Ragged last round: when the tiles fill whole rounds of resident
     // workgroups except for a few rows (at most kSkinnyMaxM), the tiled
     // kernel takes the rows of the full rounds and the weight-streaming
@@ -1148,7 +1018,7 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
     // 16384-wide layers the partial round is cheaper).
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = ((M + BM - 1) / BM) * tiles_n;
-    const int per_cu = (int)((160 * 1024) / tiled_lds_bytes<FMT>(ns, S));
+    const int per_cu = (int)((160 * 1024) / Cfg<FMT, kRing>::lds_bytes(S));
     const int slots = device_cus() * (per_cu < kBlocksPerCU ? per_cu : kBlocksPerCU);
     const int full = slots > 0 ? tiles / slots : 0;
     if (full >= 1 && tiles % slots != 0) {
@@ -1156,7 +1026,7 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
         const int tail = M - m_main;
         const int groups = (tail + 127) / 128;
         if (m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && groups * N <= kSplitMaxWidth) {
-            const hipError_t e = launch_tiled<FMT, ACC_OUT>(ns, xq, row_scale, sid, Wq, w_scale,
+            const hipError_t e = launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale,
                                                             comp_a, comp_b, m_main, N, K, S, Y,
                                                             acc_out, stream);
             if (e != hipSuccess) return e;
@@ -1167,8 +1037,8 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
                 ACC_OUT ? acc_out + (size_t)m_main * N : acc_out, stream);
         }
     }
-    return launch_tiled<FMT, ACC_OUT>(ns, xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N,
-                                      K, S, Y, acc_out, stream);
+    return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
+                                      S, Y, acc_out, stream);
 }
 
 }  // namespace
@@ -1196,15 +1066,14 @@ hipError_t launch_fused_fmt(const uint8_t* xq, const float* row_scale, const uin
                             const uint8_t* Wq, const float* w_scale, const float* comp_a,
                             const float* comp_b, int M, int N, int K, int S,
                             const NextLayerQuant& nx, hipStream_t stream) {
-    const int ns = tiled_stages<FMT>(S, 1);
     if (nx.codes == RUDDER_CODES_E2M3)
-        return launch_tiled<FMT, false, kEpiE2M3>(ns, xq, row_scale, sid, Wq, w_scale, comp_a,
+        return launch_tiled<FMT, false, kEpiE2M3>(xq, row_scale, sid, Wq, w_scale, comp_a,
                                                   comp_b, M, N, K, S, nullptr, nullptr, stream,
                                                   nx);
     if (nx.abits == 8)
-        return launch_tiled<FMT, false, kEpiQ8>(ns, xq, row_scale, sid, Wq, w_scale, comp_a,
+        return launch_tiled<FMT, false, kEpiQ8>(xq, row_scale, sid, Wq, w_scale, comp_a,
                                                 comp_b, M, N, K, S, nullptr, nullptr, stream, nx);
-    return launch_tiled<FMT, false, kEpiQ4>(ns, xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
+    return launch_tiled<FMT, false, kEpiQ4>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
                                             M, N, K, S, nullptr, nullptr, stream, nx);
 }
 

@@ -58,6 +58,11 @@ RAGGED = [
     (600, 256, 544, 2, 8, True, 6),
     (513, 1024, 256, 3, 4, True, 7),
     (97, 128, 1024, 7, 8, False, 8),
+    # tiled kernel with 1, 3 and 5 k-stages (odd stage counts end the
+    # two-stage weight/ring rotation on its first set), and 8 streams
+    (300, 128, 256, 3, 8, False, 50),
+    (301, 384, 512, 4, 4, True, 51),
+    (520, 640, 288, 8, 8, False, 52),
 ]
 
 
@@ -69,6 +74,9 @@ RAGGED_E2M3 = [
     (257, 512, 320, 3, 4, False, 13),
     (513, 1024, 256, 8, 4, True, 14),
     (97, 256, 1024, 7, 4, False, 15),
+    (300, 128, 256, 3, 4, False, 53),
+    (301, 384, 512, 8, 4, True, 54),
+    (520, 640, 288, 2, 4, False, 55),
 ]
 
 

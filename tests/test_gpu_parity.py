@@ -128,6 +128,10 @@ SMALL_M = [
     # more than 128 rows on a narrow layer: 64-row groups fill more CUs
     (192, 2048, 2048, 3, 4, False, 29, CODES_E2M3),
     (250, 512, 1024, 3, 8, True, 30, CODES_INT),
+    # wide layers: two 32-channel blocks per workgroup
+    (192, 256, 16384, 3, 4, False, 31, CODES_E2M3),
+    (250, 256, 16384, 3, 8, True, 32, CODES_INT),
+    (60, 256, 16384, 2, 4, False, 33, CODES_INT),
 ]
 
 

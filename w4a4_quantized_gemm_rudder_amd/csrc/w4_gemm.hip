@@ -700,17 +700,16 @@ constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyMaxM = 256;                 // rows handled by the small-M kernel
 constexpr int kSplitMaxWidth = 8192;             // see launch_fmt
 constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
-constexpr int kSkinnyPitch = 33;                 // LDS row pitch (words) of the sum tile
 
-// Operand registers of one k-substep: the weight fragment and up to FA
-// activation fragments, already in MFMA operand form (E2M3 fragments are
-// loaded straight into 6-dword operands).
-template <int FMT, int FA>
+// Operand registers of one k-substep: NW weight fragments (NW consecutive
+// 32-channel blocks) and up to FA activation fragments, already in MFMA
+// operand form (E2M3 fragments are loaded straight into 6-dword operands).
+template <int FMT, int FA, int NW>
 struct SkinnyOps {
     typedef typename std::conditional<FMT == kFmtF6, v6i, uint2>::type WOp;
     typedef typename std::conditional<FMT == kFmtF6, v6i,
             typename std::conditional<FMT == kFmtA8, uint4, uint2>::type>::type AOp;
-    WOp w;
+    WOp w[NW];
     AOp a[FA];
 };
 
@@ -721,15 +720,18 @@ __device__ __forceinline__ v6i load_f6_operand(const uint8_t* block, int lane) {
                                    3, 4, 5);
 }
 
-template <int FMT, int FA>
+template <int FMT, int FA, int NW>
 __device__ __forceinline__ void skinny_load(const uint8_t* __restrict__ Xq,
-                                            const uint8_t* __restrict__ Wq, int nb, int j,
+                                            const uint8_t* __restrict__ Wq, int nb0, int j,
                                             int kblocks, int mb, int lane,
-                                            SkinnyOps<FMT, FA>& op) {
+                                            SkinnyOps<FMT, FA, NW>& op) {
     using F = Fmt<FMT>;
-    const uint8_t* wblk = Wq + ((size_t)nb * kblocks + j) * F::kWBlock;
-    if constexpr (FMT == kFmtF6) op.w = load_f6_operand(wblk, lane);
-    else op.w = *reinterpret_cast<const uint2*>(wblk + lane * 8);
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        const uint8_t* wblk = Wq + ((size_t)(nb0 + i) * kblocks + j) * F::kWBlock;
+        if constexpr (FMT == kFmtF6) op.w[i] = load_f6_operand(wblk, lane);
+        else op.w[i] = *reinterpret_cast<const uint2*>(wblk + lane * 8);
+    }
 #pragma unroll
     for (int g = 0; g < FA; ++g) {
         if (g < mb) {
@@ -741,39 +743,47 @@ __device__ __forceinline__ void skinny_load(const uint8_t* __restrict__ Xq,
     }
 }
 
-template <int FMT, int FA>
-__device__ __forceinline__ void skinny_mma(const SkinnyOps<FMT, FA>& op, int mb,
-                                           typename Fmt<FMT>::Acc (&acc)[FA]) {
-    if constexpr (FMT == kFmtF6) {
+template <int FMT, int FA, int NW>
+__device__ __forceinline__ void skinny_mma(const SkinnyOps<FMT, FA, NW>& op, int mb,
+                                           typename Fmt<FMT>::Acc (&acc)[NW][FA]) {
 #pragma unroll
-        for (int g = 0; g < FA; ++g)
-            if (g < mb)
-                acc[g] = mfma_scale_f32_32x32x64_fp6(op.w, op.a[g], acc[g], 2, 2, 0, 127, 0, 127);
-    } else {
-        const v4i wf = widen_nibbles(op.w.x, op.w.y);
+    for (int i = 0; i < NW; ++i) {
+        if constexpr (FMT == kFmtF6) {
 #pragma unroll
-        for (int g = 0; g < FA; ++g) {
-            if (g < mb) {
-                v4i af;
-                if constexpr (FMT == kFmtA8)
-                    af = v4i{(int)op.a[g].x, (int)op.a[g].y, (int)op.a[g].z, (int)op.a[g].w};
-                else
-                    af = widen_nibbles(op.a[g].x, op.a[g].y);
-                acc[g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf, af, acc[g], 0, 0, 0);
+            for (int g = 0; g < FA; ++g)
+                if (g < mb)
+                    acc[i][g] = mfma_scale_f32_32x32x64_fp6(op.w[i], op.a[g], acc[i][g], 2, 2, 0,
+                                                            127, 0, 127);
+        } else {
+            const v4i wf = widen_nibbles(op.w[i].x, op.w[i].y);
+#pragma unroll
+            for (int g = 0; g < FA; ++g) {
+                if (g < mb) {
+                    v4i af;
+                    if constexpr (FMT == kFmtA8)
+                        af = v4i{(int)op.a[g].x, (int)op.a[g].y, (int)op.a[g].z, (int)op.a[g].w};
+                    else
+                        af = widen_nibbles(op.a[g].x, op.a[g].y);
+                    acc[i][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf, af, acc[i][g], 0, 0, 0);
+                }
             }
         }
     }
 }
 
-// Substeps per load chunk: every wave keeps two chunks in flight.
-template <int FMT, int FA>
+// Substeps per load chunk: every wave keeps two chunks in flight.  With two
+// weight blocks the accumulators double, so the chunk shrinks to keep the
+// operand buffers within ~200 registers with them.
+template <int FMT, int FA, int NW>
 struct SkinnyChunk {
-    static constexpr int kRegs = (FMT == kFmtF6 ? 8 : 2) +
-                                 FA * (FMT == kFmtF6 ? 8 : (FMT == kFmtA8 ? 4 : 2));
-    static constexpr int D = kRegs <= 12 ? 8 : (kRegs <= 24 ? 4 : 2);
+    static constexpr int kRegs = NW * (FMT == kFmtF6 ? 6 : 2) +
+                                 FA * (FMT == kFmtF6 ? 6 : (FMT == kFmtA8 ? 4 : 2));
+    static constexpr int kFit = (200 - 16 * NW * FA) / (2 * kRegs);
+    static constexpr int D = NW == 1 ? (kRegs <= 12 ? 8 : (kRegs <= 24 ? 4 : 2))
+                                     : (kFit >= 8 ? 8 : kFit >= 4 ? 4 : kFit >= 2 ? 2 : 1);
 };
 
-template <int FMT, int FA, bool ACC_OUT>
+template <int FMT, int FA, int NW, bool ACC_OUT>
 __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
     const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
@@ -782,19 +792,23 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
     int32_t* __restrict__ acc_out) {
     using F = Fmt<FMT>;
     using Acc = typename F::Acc;
+    constexpr int NC = NW * 32;                    // channels of this workgroup
+    constexpr int kPitch = NC + 1;                 // LDS row pitch (words) of the sum tile
+    constexpr int kTabMax = NC * (1 + 2 * RUDDER_MAX_STREAMS);
+    constexpr int kTabPer = (kTabMax + kSkinnyThreads - 1) / kSkinnyThreads;
     static_assert(FA * 32 <= kSkinnyThreads, "one thread per row for the row data");
     // exact integer dot products, summed as int32 (fp32 partials of the
     // E2M3 path are integers below 2^24 and convert exactly)
-    __shared__ int sum[FA * 32 * kSkinnyPitch];
-    // per-block epilogue operands: w_scale[32], comp_a[S][32], comp_b[S][32]
-    __shared__ float tab[32 + 64 * RUDDER_MAX_STREAMS];
+    __shared__ int sum[FA * 32 * kPitch];
+    // per-block epilogue operands: w_scale[NC], comp_a[S][NC], comp_b[S][NC]
+    __shared__ float tab[kTabMax];
     __shared__ float rows_rs[FA * 32];
     __shared__ int rows_s[FA * 32];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nb = blockIdx.x;                     // 32-channel block
+    const int nb0 = blockIdx.x * NW;               // first 32-channel block
     const int kblocks = K / F::kKSub;
     // this workgroup's rows: group blockIdx.y of FA * 32 rows
     {
@@ -808,46 +822,53 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
     }
     const int mb = (M + 31) >> 5;                  // 32-row blocks present (<= FA)
 
-    for (int i = tid; i < FA * 32 * kSkinnyPitch; i += kSkinnyThreads) sum[i] = 0;
+    for (int i = tid; i < FA * 32 * kPitch; i += kSkinnyThreads) sum[i] = 0;
 
     // epilogue operands: fetched now (in flight with the k loop), written to
     // LDS after it
-    const int ntab = 32 + 64 * S;
+    const int ntab = NC * (1 + 2 * S);
     auto tab_src = [&](int i) -> const float* {
-        if (i < 32) return w_scale + nb * 32 + i;
-        i -= 32;
-        const int half = i / (32 * S);             // 0: comp_a, 1: comp_b
-        i -= half * 32 * S;
-        return (half ? comp_b : comp_a) + (size_t)(i >> 5) * N + nb * 32 + (i & 31);
+        if (i < NC) return w_scale + nb0 * 32 + i;
+        i -= NC;
+        const int half = i / (NC * S);             // 0: comp_a, 1: comp_b
+        i -= half * NC * S;
+        return (half ? comp_b : comp_a) + (size_t)(i / NC) * N + nb0 * 32 + (i % NC);
     };
-    const float e_tab0 = tid < ntab ? *tab_src(tid) : 0.0f;
-    const float e_tab1 = tid + kSkinnyThreads < ntab ? *tab_src(tid + kSkinnyThreads) : 0.0f;
+    float e_tab[kTabPer];
+#pragma unroll
+    for (int t = 0; t < kTabPer; ++t) {
+        const int i = tid + t * kSkinnyThreads;
+        e_tab[t] = i < ntab ? *tab_src(i) : 0.0f;
+    }
     const float e_rs = tid < M ? row_scale[tid] : 0.0f;
     const int e_s = tid < M ? min(sid[tid] & (RUDDER_MAX_STREAMS - 1), S - 1) : 0;
 
-    Acc acc[FA];
+    Acc acc[NW][FA];
 #pragma unroll
-    for (int g = 0; g < FA; ++g)
+    for (int i = 0; i < NW; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[g][r] = 0;
+        for (int g = 0; g < FA; ++g)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][g][r] = 0;
 
     // Each wave takes a contiguous range of k-substeps and walks it in chunks
     // of D substeps; the loads of chunk c+1 are issued before the MFMAs of
     // chunk c, so two chunks (the whole range for short K) are in flight.
-    constexpr int D = SkinnyChunk<FMT, FA>::D;
+    constexpr int D = SkinnyChunk<FMT, FA, NW>::D;
     const int per_wave = (kblocks + kSkinnyWaves - 1) / kSkinnyWaves;
     const int j0 = wave * per_wave;
     const int j1 = min(j0 + per_wave, kblocks);
-    SkinnyOps<FMT, FA> ops[2][D];
-    auto load_chunk = [&](int jc, SkinnyOps<FMT, FA>(&buf)[D]) {
+    SkinnyOps<FMT, FA, NW> ops[2][D];
+    auto load_chunk = [&](int jc, SkinnyOps<FMT, FA, NW>(&buf)[D]) {
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (jc + d < j1) skinny_load<FMT, FA>(Xq, Wq, nb, jc + d, kblocks, mb, lane, buf[d]);
+            if (jc + d < j1)
+                skinny_load<FMT, FA, NW>(Xq, Wq, nb0, jc + d, kblocks, mb, lane, buf[d]);
     };
-    auto mma_chunk = [&](int jc, const SkinnyOps<FMT, FA>(&buf)[D]) {
+    auto mma_chunk = [&](int jc, const SkinnyOps<FMT, FA, NW>(&buf)[D]) {
 #pragma unroll
         for (int d = 0; d < D; ++d)
-            if (jc + d < j1) skinny_mma<FMT, FA>(buf[d], mb, acc);
+            if (jc + d < j1) skinny_mma<FMT, FA, NW>(buf[d], mb, acc);
     };
     if (j0 < j1) load_chunk(j0, ops[0]);
     for (int jc = j0; jc < j1; jc += 2 * D) {
@@ -858,44 +879,51 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
             mma_chunk(jc + D, ops[1]);
         }
     }
-    if (tid < ntab) tab[tid] = e_tab0;
-    if (tid + kSkinnyThreads < ntab) tab[tid + kSkinnyThreads] = e_tab1;
+#pragma unroll
+    for (int t = 0; t < kTabPer; ++t) {
+        const int i = tid + t * kSkinnyThreads;
+        if (i < ntab) tab[i] = e_tab[t];
+    }
     if (tid < FA * 32) {
         rows_rs[tid] = e_rs;
         rows_s[tid] = e_s;
     }
     __syncthreads();                               // sum tile cleared, operands in LDS
 
-    // partial sums -> LDS tile [row][channel] (row pitch 33 words)
+    // partial sums -> LDS tile [row][channel] (row pitch NC + 1 words)
 #pragma unroll
-    for (int g = 0; g < FA; ++g) {
-        if (g < mb) {
-            const int m = g * 32 + (lane & 31);
+    for (int i = 0; i < NW; ++i) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int n = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                atomicAdd(&sum[m * kSkinnyPitch + n], (int)acc[g][r]);
+        for (int g = 0; g < FA; ++g) {
+            if (g < mb) {
+                const int m = g * 32 + (lane & 31);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int n = 32 * i + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    atomicAdd(&sum[m * kPitch + n], (int)acc[i][g][r]);
+                }
             }
         }
     }
     __syncthreads();
 
-    // epilogue: item = (row m, 8-channel group c); 4 items per row
-    for (int item = tid; item < mb * 32 * 4; item += kSkinnyThreads) {
-        const int m = item >> 2;
-        const int c = item & 3;
+    // epilogue: item = (row m, 8-channel group c); NC / 8 items per row
+    constexpr int kGroups = NC / 8;
+    for (int item = tid; item < mb * 32 * kGroups; item += kSkinnyThreads) {
+        const int m = item / kGroups;
+        const int c = item % kGroups;
         if (m >= M) continue;
-        const int n0 = nb * 32 + c * 8;
+        const int n0 = nb0 * 32 + c * 8;
         const int st = rows_s[m];
         const float rs = rows_rs[m];
         const float* ws = tab + c * 8;
-        const float* a = tab + 32 + st * 32 + c * 8;
-        const float* b = tab + 32 + 32 * S + st * 32 + c * 8;
+        const float* a = tab + NC + st * NC + c * 8;
+        const float* b = tab + NC + NC * S + st * NC + c * 8;
         int v[8];
         float y[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int w = sum[m * kSkinnyPitch + c * 8 + i];
+            const int w = sum[m * kPitch + c * 8 + i];
             if constexpr (FMT == kFmtF6) v[i] = w;
             else if constexpr (FMT == kFmtA8) v[i] = w >> 4;
             else v[i] = w >> 8;
@@ -915,16 +943,27 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
         }
     }
 }
+int device_cus();
 
+// NW = 2 (64 channels per workgroup) halves the activation re-reads, which
+// dominate the L2 traffic of this kernel, whenever the grid still covers
+// every compute unit.
 template <int FMT, int FA, bool ACC_OUT>
 hipError_t launch_skinny(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
                          const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                          int32_t* acc_out, hipStream_t stream) {
     const unsigned row_groups = (unsigned)((M + FA * 32 - 1) / (FA * 32));
-    hipLaunchKernelGGL((w4_skinny_kernel<FMT, FA, ACC_OUT>), dim3((unsigned)(N / 32), row_groups),
-                       dim3(kSkinnyThreads), 0, stream, xq, row_scale, sid, Wq, w_scale, comp_a,
-                       comp_b, M, N, K, S, Y, acc_out);
+    if (N % 64 == 0 && (N / 64) * (int)row_groups >= device_cus())
+        hipLaunchKernelGGL((w4_skinny_kernel<FMT, FA, 2, ACC_OUT>),
+                           dim3((unsigned)(N / 64), row_groups), dim3(kSkinnyThreads), 0, stream,
+                           xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S, Y,
+                           acc_out);
+    else
+        hipLaunchKernelGGL((w4_skinny_kernel<FMT, FA, 1, ACC_OUT>),
+                           dim3((unsigned)(N / 32), row_groups), dim3(kSkinnyThreads), 0, stream,
+                           xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S, Y,
+                           acc_out);
     return hipGetLastError();
 }
 

@@ -206,6 +206,11 @@ __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, uint
 // vector-memory loads are in flight, then barrier the workgroup: afterwards
 // every wave's loads up to that point have landed in LDS, and no wave still
 // reads the buffer that the next loads overwrite.
+// s_waitcnt immediate (gfx9 layout: vmcnt bits 3..0 and 15..14, expcnt 6..4,
+// lgkmcnt 11..8) that waits for LDS / scalar-memory results only:
+// vmcnt = 63 and expcnt = 7 (no wait), lgkmcnt = 0.
+constexpr int kWaitLgkm0 = 0xC07F;
+
 template <int N>
 __device__ __forceinline__ void wait_and_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -481,7 +486,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             // reads, carry no wait on those reads.
             mma(wreg[u][kk], fa[kk % 2], 0, 1);
             asm volatile("" : "+v"(acc[0][0]));
-            __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0) only
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
             if (kk + 1 < P) {
                 read_acts(kt, kk + 1, fa[(kk + 1) % 2]);
             } else if (kt < klast) {

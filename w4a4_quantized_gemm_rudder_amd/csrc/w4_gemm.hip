@@ -174,6 +174,14 @@ __device__ __forceinline__ v4i widen_nibbles(uint32_t w0, uint32_t w1) {
     return r;
 }
 
+// 16-byte store of the bf16 output with the streaming (non-temporal) hint:
+// the output tiles are written once and are far larger than L2, so they
+// should not evict the weight and activation panels other tiles still read.
+__device__ __forceinline__ void store_y16(uint16_t* p, uint4 v) {
+    typedef unsigned v4u __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
+}
+
 // Two fp32 -> packed bf16 with round-to-nearest-even (gfx950 hardware
 // conversion; finite inputs): low half = a, high half = b.
 __device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
@@ -684,7 +692,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         const uint4 v =
             *reinterpret_cast<const uint4*>(wstage + r * kWaveRowBytes + ((c ^ swz(r)) * 16));
         if (m0 + r < M && n < N)
-            *reinterpret_cast<uint4*>(Y + (size_t)(m0 + r) * N + n) = v;
+            store_y16(Y + (size_t)(m0 + r) * N + n, v);
     }
 }
 
@@ -939,7 +947,7 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
         out.y = pack_bf16x2_rne(y[2], y[3]);
         out.z = pack_bf16x2_rne(y[4], y[5]);
         out.w = pack_bf16x2_rne(y[6], y[7]);
-        *reinterpret_cast<uint4*>(Y + (size_t)m * N + n0) = out;
+        store_y16(Y + (size_t)m * N + n0, out);
         if constexpr (ACC_OUT) {
             *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n0) =
                 make_int4(v[0], v[1], v[2], v[3]);

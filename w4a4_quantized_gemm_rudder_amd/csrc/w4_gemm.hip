@@ -281,6 +281,14 @@ __device__ __forceinline__ int acc_value(const typename Fmt<FMT>::Acc& a, int r)
     else return a[r] >> 8;
 }
 
+// The same value as an fp32 (exact: |acc| < 2^24).  The E2M3 accumulators
+// already hold it; the int containers shift and convert.
+template <int FMT>
+__device__ __forceinline__ float acc_float(const typename Fmt<FMT>::Acc& a, int r) {
+    if constexpr (FMT == kFmtF6) return a[r];
+    else return (float)acc_value<FMT>(a, r);
+}
+
 template <int FMT, int NS, bool ACC_OUT, int EPI>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
@@ -414,17 +422,18 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         wblk[f] = Wq + (size_t)gnb * kblocks * F::kWBlock;
     }
     const uint32_t off0 = lane * (kF6 ? 16 : 8), off1 = 1024 + lane * 8;
-    auto load_w = [&](int kt, int kk, WOp (&dst)[FW]) {
+    auto load_w = [&](int kt, int kk, WOp (&dst)[FW], bool real = true) {
+        const uint32_t o0 = real ? off0 : 0u, o1 = real ? off1 : 0u;
 #pragma unroll
         for (int f = 0; f < FW; ++f) {
             const uint8_t* b = wblk[f] + (size_t)(kt * P + kk) * F::kWBlock;
             if constexpr (kF6) {
-                const v4i p0 = *reinterpret_cast<const v4i*>(b + off0);
-                const v2i p1 = *reinterpret_cast<const v2i*>(b + off1);
+                const v4i p0 = *reinterpret_cast<const v4i*>(b + o0);
+                const v2i p1 = *reinterpret_cast<const v2i*>(b + o1);
                 dst[f] = __builtin_shufflevector(
                     p0, __builtin_shufflevector(p1, p1, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5);
             } else {
-                dst[f] = *reinterpret_cast<const uint2*>(b + off0);
+                dst[f] = *reinterpret_cast<const uint2*>(b + o0);
             }
         }
     };
@@ -464,10 +473,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     // Prologue, in this order: ring stages 0 and 1, then the weights of
     // stages 0 and 1.  vmcnt counts in issue order; a wait for a ring stage
     // leaves outstanding only what was issued after it.  Weight loads are
-    // issued unconditionally (past the last stage they re-read the last
-    // stage's blocks into a slot that is not used again), which keeps the
-    // counts below fixed and the compiler's own waits for the weight
-    // registers exact.
+    // issued unconditionally, which keeps the counts below fixed and the
+    // compiler's own waits for the weight registers exact: past the last
+    // stage a refill becomes a dummy load that every lane points at the
+    // block's first 16 bytes (one cache line per instruction, nothing
+    // left to prefetch), into a slot that is not read again.
     constexpr int LA = C::kActLoads;
     WOp wreg[2][P][FW];
     AOp fa[2][FA];
@@ -485,6 +495,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     // One stage; u = kt % 2 selects the weight register set.
     auto stage = [&](int kt, auto u_) {
         constexpr int u = decltype(u_)::value;
+        const bool prefetch = kt + 2 <= klast;     // stage kt+2 exists
 #pragma unroll
         for (int kk = 0; kk < P; ++kk) {
             // The substep's first MFMA goes ahead of the next reads.  It
@@ -513,7 +524,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             for (int f = 0; f < FW; ++f)
 #pragma unroll
                 for (int g = 0; g < FA; ++g) asm volatile("" : "+v"(acc[f][g]));
-            load_w(min(kt + 2, klast), kk, wreg[u][kk]);
+            load_w(min(kt + 2, klast), kk, wreg[u][kk], prefetch);
         }
     };
     int kt = 0;
@@ -549,70 +560,120 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     }
     const int tab_shift = tile_n * BN - (N >= BN ? min(n_tile0, N - BN) : 0);
     uint8_t* wstage = lds + wave * (kWaveRows * kWaveRowBytes);
+    // When every token row of the wave belongs to one stream (the usual case:
+    // rows come stream by stream), the comp rows a[s], b[s] are read once per
+    // channel quad instead of once per 32-token block.
+    const int s_first = __builtin_amdgcn_readfirstlane(row_stream[0]);
+    bool one_stream = true;
 #pragma unroll
-    for (int f = 0; f < FW; ++f) {
+    for (int g = 0; g < FA; ++g) one_stream = one_stream && row_stream[g] == s_first;
+    const bool wave_one_stream = __builtin_amdgcn_ballot_w64(!one_stream) == 0;
+    // channel quad (f, q) of this lane, and its column in the table window
+    auto table_col = [&](int f, int q) {
+        return min(wn * (FW * 32) + f * 32 + 8 * q + 4 * (lane >> 5) + tab_shift, 252);
+    };
+    auto stage_tile = [&](auto uniform_) {
+        constexpr bool kUniform = decltype(uniform_)::value;
+        // one stream, bf16 output: every table value the wave needs, read up
+        // front in one batch (the fragment registers of the k loop are free
+        // by now; the code epilogues have no room for it)
+        constexpr bool kPreload = kUniform && EPI == kEpiBf16;
+        float4 pw[FW][4], pa[FW][4], pb[FW][4];
+        if constexpr (kPreload) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int nl = wn * (FW * 32) + f * 32 + 8 * q + 4 * (lane >> 5);  // channel in tile
-            const int ti = min(nl + tab_shift, 252);           // column in the table window
-            const float4 ws = *reinterpret_cast<const float4*>(tab + ti);
-            const int chunk = f * 4 + q;                       // 16-byte chunk in the wave row
+            for (int f = 0; f < FW; ++f)
 #pragma unroll
-            for (int g = 0; g < FA; ++g) {
-                const int s = row_stream[g];
-                const float rs = row_rs[g];
-                const float4 a = *reinterpret_cast<const float4*>(tab + 256 * (1 + s) + ti);
-                const float4 b = *reinterpret_cast<const float4*>(tab + 256 * (1 + S + s) + ti);
-                const int v0 = acc_value<FMT>(acc[f][g], 4 * q + 0);
-                const int v1 = acc_value<FMT>(acc[f][g], 4 * q + 1);
-                const int v2 = acc_value<FMT>(acc[f][g], 4 * q + 2);
-                const int v3 = acc_value<FMT>(acc[f][g], 4 * q + 3);
-                const float y0 = __builtin_fmaf(a.x, (float)v0 * (rs * ws.x), b.x);
-                const float y1 = __builtin_fmaf(a.y, (float)v1 * (rs * ws.y), b.y);
-                const float y2 = __builtin_fmaf(a.z, (float)v2 * (rs * ws.z), b.z);
-                const float y3 = __builtin_fmaf(a.w, (float)v3 * (rs * ws.w), b.w);
-                uint2 packed;
-                packed.x = pack_bf16x2_rne(y0, y1);
-                packed.y = pack_bf16x2_rne(y2, y3);
-                const int r = g * 32 + (lane & 31);
-                if constexpr (EPI == kEpiBf16) {
-                    *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes + ((chunk ^ swz(r)) * 16) +
-                                              (lane >> 5) * 8) = packed;
-                } else {
-                    // GELU of the bf16 values, then the next layer's quantizer:
-                    // u = gelu * inv_smooth'[n]; q = rne(clamp(u * (1/D'[s])))
-                    const float4 ni =
-                        *reinterpret_cast<const float4*>(tab + 256 * (1 + 2 * S) + ti);
-                    const float g0 = bf16_bits_to_float(kGeluBf16[packed.x & 0xFFFFu]);
-                    const float g1 = bf16_bits_to_float(kGeluBf16[packed.x >> 16]);
-                    const float g2 = bf16_bits_to_float(kGeluBf16[packed.y & 0xFFFFu]);
-                    const float g3 = bf16_bits_to_float(kGeluBf16[packed.y >> 16]);
-                    const float ia = next_ia[g];
-                    const uint32_t word =
-                        ((uint32_t)quantize_clamped((g0 * ni.x) * ia, kQNext) & 0xFFu) |
-                        (((uint32_t)quantize_clamped((g1 * ni.y) * ia, kQNext) & 0xFFu) << 8) |
-                        (((uint32_t)quantize_clamped((g2 * ni.z) * ia, kQNext) & 0xFFu) << 16) |
-                        (((uint32_t)quantize_clamped((g3 * ni.w) * ia, kQNext) & 0xFFu) << 24);
-                    // code staging: row r of the wave, 64 one-byte codes, 16-byte
-                    // chunk k16 stored at chunk k16 ^ (r & 3)
-                    *reinterpret_cast<uint32_t*>(
-                        wstage + r * kCodeRowBytes +
-                        (((f * 2 + (q >> 1)) ^ (r & 3)) * 16) + 8 * (q & 1) + 4 * (lane >> 5)) =
-                        word;
+                for (int q = 0; q < 4; ++q) {
+                    const int ti = table_col(f, q);
+                    pw[f][q] = *reinterpret_cast<const float4*>(tab + ti);
+                    pa[f][q] = *reinterpret_cast<const float4*>(tab + 256 * (1 + s_first) + ti);
+                    pb[f][q] =
+                        *reinterpret_cast<const float4*>(tab + 256 * (1 + S + s_first) + ti);
                 }
-                if constexpr (ACC_OUT) {
-                    const int m = tile_m * BM + wm * kWaveRows + r;
-                    const int n = tile_n * BN + nl;
-                    if (m < M && n < N)
-                        *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n) =
-                            make_int4(v0, v1, v2, v3);
+        }
+#pragma unroll
+        for (int f = 0; f < FW; ++f) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = wn * (FW * 32) + f * 32 + 8 * q + 4 * (lane >> 5);  // in the tile
+                const int ti = table_col(f, q);
+                const float4 ws =
+                    kPreload ? pw[f][q] : *reinterpret_cast<const float4*>(tab + ti);
+                const int chunk = f * 4 + q;                       // 16-byte chunk in the wave row
+                if constexpr (kUniform && !kPreload) {
+                    pa[f][q] = *reinterpret_cast<const float4*>(tab + 256 * (1 + s_first) + ti);
+                    pb[f][q] =
+                        *reinterpret_cast<const float4*>(tab + 256 * (1 + S + s_first) + ti);
+                }
+#pragma unroll
+                for (int g = 0; g < FA; ++g) {
+                    const int s = row_stream[g];
+                    const float rs = row_rs[g];
+                    float4 a, b;
+                    if constexpr (kUniform) {
+                        a = pa[f][q];
+                        b = pb[f][q];
+                    } else {
+                        a = *reinterpret_cast<const float4*>(tab + 256 * (1 + s) + ti);
+                        b = *reinterpret_cast<const float4*>(tab + 256 * (1 + S + s) + ti);
+                    }
+                    const float t0 = acc_float<FMT>(acc[f][g], 4 * q + 0) * (rs * ws.x);
+                    const float t1 = acc_float<FMT>(acc[f][g], 4 * q + 1) * (rs * ws.y);
+                    const float t2 = acc_float<FMT>(acc[f][g], 4 * q + 2) * (rs * ws.z);
+                    const float t3 = acc_float<FMT>(acc[f][g], 4 * q + 3) * (rs * ws.w);
+                    const float y0 = __builtin_fmaf(a.x, t0, b.x);
+                    const float y1 = __builtin_fmaf(a.y, t1, b.y);
+                    const float y2 = __builtin_fmaf(a.z, t2, b.z);
+                    const float y3 = __builtin_fmaf(a.w, t3, b.w);
+                    uint2 packed;
+                    packed.x = pack_bf16x2_rne(y0, y1);
+                    packed.y = pack_bf16x2_rne(y2, y3);
+                    const int r = g * 32 + (lane & 31);
+                    if constexpr (EPI == kEpiBf16) {
+                        *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes +
+                                                  ((chunk ^ swz(r)) * 16) + (lane >> 5) * 8) =
+                            packed;
+                    } else {
+                        // GELU of the bf16 values, then the next layer's quantizer:
+                        // u = gelu * inv_smooth'[n]; q = rne(clamp(u * (1/D'[s])))
+                        const float4 ni =
+                            *reinterpret_cast<const float4*>(tab + 256 * (1 + 2 * S) + ti);
+                        const float g0 = bf16_bits_to_float(kGeluBf16[packed.x & 0xFFFFu]);
+                        const float g1 = bf16_bits_to_float(kGeluBf16[packed.x >> 16]);
+                        const float g2 = bf16_bits_to_float(kGeluBf16[packed.y & 0xFFFFu]);
+                        const float g3 = bf16_bits_to_float(kGeluBf16[packed.y >> 16]);
+                        const float ia = next_ia[g];
+                        const uint32_t word =
+                            ((uint32_t)quantize_clamped((g0 * ni.x) * ia, kQNext) & 0xFFu) |
+                            (((uint32_t)quantize_clamped((g1 * ni.y) * ia, kQNext) & 0xFFu) << 8) |
+                            (((uint32_t)quantize_clamped((g2 * ni.z) * ia, kQNext) & 0xFFu) << 16) |
+                            (((uint32_t)quantize_clamped((g3 * ni.w) * ia, kQNext) & 0xFFu) << 24);
+                        // code staging: row r of the wave, 64 one-byte codes, 16-byte
+                        // chunk k16 stored at chunk k16 ^ (r & 3)
+                        *reinterpret_cast<uint32_t*>(
+                            wstage + r * kCodeRowBytes +
+                            (((f * 2 + (q >> 1)) ^ (r & 3)) * 16) + 8 * (q & 1) + 4 * (lane >> 5)) =
+                            word;
+                    }
+                    if constexpr (ACC_OUT) {
+                        const int m = tile_m * BM + wm * kWaveRows + r;
+                        const int n = tile_n * BN + nl;
+                        if (m < M && n < N)
+                            *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n) =
+                                make_int4(acc_value<FMT>(acc[f][g], 4 * q + 0),
+                                          acc_value<FMT>(acc[f][g], 4 * q + 1),
+                                          acc_value<FMT>(acc[f][g], 4 * q + 2),
+                                          acc_value<FMT>(acc[f][g], 4 * q + 3));
+                    }
                 }
             }
+            // keep the accumulator reads of one fragment column together
+            // (bounds the registers the epilogue needs)
+            __builtin_amdgcn_sched_barrier(0);
         }
-        // keep the accumulator reads of one fragment column together
-        // (bounds the registers the epilogue needs)
-        __builtin_amdgcn_sched_barrier(0);
-    }
+    };
+    if (wave_one_stream) stage_tile(std::true_type{});
+    else stage_tile(std::false_type{});
     if constexpr (EPI != kEpiBf16) {
         // 2'. the next layer's packed codes from the staged bytes (this wave's
         //     128 rows x 64 channels; rows M .. ceil32(M) - 1 get code 0) and
@@ -682,17 +743,23 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     }
     // 2. whole-line stores of this wave's rows (its own LDS writes are
     //    ordered before these reads)
+    //    All of the wave's staged rows are read back first (one LDS round
+    //    trip), then stored.
     constexpr int kRowsPerStore = 64 / kRowChunks;
+    constexpr int kStores = kWaveRows / kRowsPerStore;
     const int c = lane & (kRowChunks - 1);
     const int m0 = tile_m * BM + wm * kWaveRows;
     const int n = tile_n * BN + wn * (FW * 32) + c * 8;
-#pragma unroll 4
-    for (int i = 0; i < kWaveRows / kRowsPerStore; ++i) {
+    uint4 out[kStores];
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {
         const int r = i * kRowsPerStore + lane / kRowChunks;
-        const uint4 v =
-            *reinterpret_cast<const uint4*>(wstage + r * kWaveRowBytes + ((c ^ swz(r)) * 16));
-        if (m0 + r < M && n < N)
-            store_y16(Y + (size_t)(m0 + r) * N + n, v);
+        out[i] = *reinterpret_cast<const uint4*>(wstage + r * kWaveRowBytes + ((c ^ swz(r)) * 16));
+    }
+#pragma unroll
+    for (int i = 0; i < kStores; ++i) {
+        const int r = i * kRowsPerStore + lane / kRowChunks;
+        if (m0 + r < M && n < N) store_y16(Y + (size_t)(m0 + r) * N + n, out[i]);
     }
 }
 

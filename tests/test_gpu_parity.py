@@ -157,6 +157,39 @@ def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
 
 
+# Rows in runs of one stream, as the workloads order them.  The tiled
+# epilogue takes a batched path when all 128 token rows of a wave share one
+# stream and a per-row gather otherwise; the runs below give both kinds of
+# wave in one call: whole 128-row waves of one stream, run boundaries inside
+# a wave and on a wave boundary, a single row of another stream inside a run,
+# and a ragged last tile.
+@pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3)])
+def test_stream_runs_uniform_and_mixed_waves(abits, codes):
+    M, K, N, S = 700, 256, 512, 4
+    rng = np.random.default_rng(60 + abits + codes)
+    sid = np.zeros(M, np.uint8)
+    sid[128:192] = 1          # boundary inside the second wave of tile 0
+    sid[192:256] = 2
+    sid[256:384] = 2          # a whole wave of stream 2
+    sid[384:512] = 3
+    sid[450] = 0              # one foreign row inside a stream-3 wave
+    sid[512:640] = 1
+    sid[640:] = 2             # ragged last tile
+    x = rng.standard_normal((M, K))
+    x[:, rng.integers(0, K, 3)] *= 25.0
+    X = _torch_bf16_bits(x)
+    Wb = _torch_bf16_bits(rng.standard_normal((K, N)) * 0.02)
+    s = rng.uniform(0.25, 4.0, K).astype(np.float32)
+    a = rng.uniform(0.9, 1.1, (S, N)).astype(np.float32)
+    b = (rng.standard_normal((S, N)) * 0.01).astype(np.float32)
+    qa = 127 if abits == 8 else 7
+    delta = (rng.uniform(0.5, 1.0, S) * np.abs(x / s[None, :]).max() / qa).astype(np.float32)
+    log(f"case stream runs M={M} K={K} N={N} S={S} abits={abits} codes={codes}")
+    run = LayerRun(X, sid, Wb, s, a, b, S, abits, codes)
+    run.check_weights()
+    log(f"  {run.run_step(delta, a, b, label='runs')}")
+
+
 @pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3)])
 def test_saturated_codes_at_max_k(abits, codes):
     """K = 65536 (the largest supported) with every weight and activation code

@@ -157,6 +157,21 @@ def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
 
 
+# Wider layers with the int containers: the rows past the last whole round
+# run as half-width (128-channel) tiles in the same launch.  8192 + 192 rows
+# x 6144 channels = 1584 tiles of 128 x 256 for 512 resident workgroups;
+# 8192 + 100 rows x 12288 channels; one and two k-stages.  Every row is
+# compared.
+@pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes", [
+    (8384, 128, 6144, 3, 8, False, 44, CODES_INT),
+    (8384, 256, 6144, 3, 4, True, 45, CODES_INT),
+    (8292, 128, 12288, 4, 8, False, 46, CODES_INT),
+])
+def test_round_remainder_narrow_tiles(M, K, N, S, abits, dynamic, seed, codes):
+    log(f"case narrow tail M={M} K={K} N={N} S={S} abits={abits} codes={codes}")
+    log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
+
+
 # Rows in runs of one stream, as the workloads order them.  The tiled
 # epilogue takes a batched path when all 128 token rows of a wave share one
 # stream and a per-row gather otherwise; the runs below give both kinds of

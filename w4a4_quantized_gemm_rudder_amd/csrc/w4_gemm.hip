@@ -133,16 +133,16 @@ struct Fmt<kFmtF6> {
     typedef v16f Acc;
 };
 
-template <int FMT>
+template <int FMT, int TBN = BN>
 struct Waves {
     static constexpr int kN = Fmt<FMT>::kWavesN;          // waves along channels
     static constexpr int kM = kWaves / kN;                // waves along tokens
-    static constexpr int FW = BN / kN / 32;               // 32-channel fragments per wave
+    static constexpr int FW = TBN / kN / 32;              // 32-channel fragments per wave
     static constexpr int FA = BM / kM / 32;               // 32-token fragments per wave
-    static_assert(kN * kM == kWaves && FW * kN * 32 == BN && FA * kM * 32 == BM, "wave grid");
+    static_assert(kN * kM == kWaves && FW * kN * 32 == TBN && FA * kM * 32 == BM, "wave grid");
 };
 
-template <int FMT, int NS>
+template <int FMT, int NS, int TBN = BN>
 struct Cfg {
     using F = Fmt<FMT>;
     static constexpr int kActBlock = F::kABlock;
@@ -153,7 +153,7 @@ struct Cfg {
     static constexpr int kRingBytes = NS * kStageBytes;
     // 16-byte direct loads per thread per stage (each wave instruction = 1 KiB)
     static constexpr int kActLoads = kActBytes / (1024 * kWaves);
-    static constexpr int kEpiBytes = BM * BN * 2;                    // bf16 tile
+    static constexpr int kEpiBytes = BM * TBN * 2;                   // bf16 tile
     // Per-tile epilogue tables (w_scale, comp_a[S], comp_b[S] for the tile's
     // 256 channels, 1 KiB each) live after both the ring and the bf16 tile.
     static constexpr int kTableOffset = kRingBytes > kEpiBytes ? kRingBytes : kEpiBytes;
@@ -289,17 +289,20 @@ __device__ __forceinline__ float acc_float(const typename Fmt<FMT>::Acc& a, int 
     else return (float)acc_value<FMT>(a, r);
 }
 
-template <int FMT, int NS, bool ACC_OUT, int EPI>
-__global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
+// One block tile: rows tile_m * BM .. + BM - 1, channels tile_n * TBN ..
+// + TBN - 1 (TBN = BN, or BN / 2 for the narrow tiles of a ragged last
+// round).
+template <int FMT, int NS, bool ACC_OUT, int EPI, int TBN>
+__device__ __forceinline__ void gemm_tile(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
     const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
-    int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, NextLayerQuant nx) {
-    using C = Cfg<FMT, NS>;
+    int32_t* __restrict__ acc_out, int tile_m, int tile_n, const NextLayerQuant& nx) {
+    using C = Cfg<FMT, NS, TBN>;
     using F = Fmt<FMT>;
-    constexpr int FW = Waves<FMT>::FW, FA = Waves<FMT>::FA;
-    constexpr int kWavesN = Waves<FMT>::kN;
+    constexpr int FW = Waves<FMT, TBN>::FW, FA = Waves<FMT, TBN>::FA;
+    constexpr int kWavesN = Waves<FMT, TBN>::kN;
     extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
 
     const int tid = threadIdx.x;
@@ -309,13 +312,11 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const int wm = wave / kWavesN;    // token slice of the tile (FA * 32 tokens)
     const int uwave = __builtin_amdgcn_readfirstlane(wave);   // wave index as a scalar
 
-    int tile_m, tile_n;
-    tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tile_m, tile_n);
     const int kblocks = K / F::kKSub;                       // code blocks along k
     const int mblocks = (M + 31) >> 5;
     const int nblocks = N >> 5;
     const int ksteps = K / BK;
-    const int n_tile0 = min(tile_n * BN, N - 32);            // first channel of the tile (clamped)
+    const int n_tile0 = min(tile_n * TBN, N - 32);           // first channel of the tile (clamped)
 
     // Stream id and row scale of this lane's FA token rows (plain loads; the
     // compiler waits for them only in the epilogue).  The int formats fetch
@@ -418,7 +419,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const int uwn = uwave % kWavesN;
 #pragma unroll
     for (int f = 0; f < FW; ++f) {
-        const int gnb = min(tile_n * (BN / 32) + uwn * FW + f, nblocks - 1);
+        const int gnb = min(tile_n * (TBN / 32) + uwn * FW + f, nblocks - 1);
         wblk[f] = Wq + (size_t)gnb * kblocks * F::kWBlock;
     }
     const uint32_t off0 = lane * (kF6 ? 16 : 8), off1 = 1024 + lane * 8;
@@ -543,11 +544,13 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     //    the LDS tables.
     // 2. each wave stores its own rows: FW*4 lanes per row (128 or 256
     //    bytes), so every store instruction writes whole cache lines.
-    constexpr int kWaveRowBytes = FW * 32 * 2;                 // 128 or 256
+    constexpr int kWaveRowBytes = FW * 32 * 2;                 // 64, 128 or 256
     constexpr int kWaveRows = FA * 32;                         // 128 or 64
-    constexpr int kRowChunks = kWaveRowBytes / 16;             // 8 or 16
+    constexpr int kRowChunks = kWaveRowBytes / 16;             // 4, 8 or 16
     if constexpr (kLateRowData) fetch_row_data();
-    auto swz = [](int r) { return kRowChunks == 8 ? ((r >> 1) & 7) : (r & 15); };
+    auto swz = [](int r) {
+        return kRowChunks == 4 ? ((r >> 1) & 3) : (kRowChunks == 8 ? ((r >> 1) & 7) : (r & 15));
+    };
     __syncthreads();                                   // ring no longer read
     const float* tab = reinterpret_cast<const float*>(lds + C::kTableOffset);
     // next-layer quantizer (code epilogues): reciprocal step per row, Qa
@@ -558,7 +561,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
 #pragma unroll
         for (int g = 0; g < FA; ++g) next_ia[g] = step_reciprocal(nx.delta[row_stream[g]]);
     }
-    const int tab_shift = tile_n * BN - (N >= BN ? min(n_tile0, N - BN) : 0);
+    const int tab_shift = tile_n * TBN - (N >= BN ? min(n_tile0, N - BN) : 0);
     uint8_t* wstage = lds + wave * (kWaveRows * kWaveRowBytes);
     // When every token row of the wave belongs to one stream (the usual case:
     // rows come stream by stream), the comp rows a[s], b[s] are read once per
@@ -657,7 +660,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
                     }
                     if constexpr (ACC_OUT) {
                         const int m = tile_m * BM + wm * kWaveRows + r;
-                        const int n = tile_n * BN + nl;
+                        const int n = tile_n * TBN + nl;
                         if (m < M && n < N)
                             *reinterpret_cast<int4*>(acc_out + (size_t)m * N + n) =
                                 make_int4(acc_value<FMT>(acc[f][g], 4 * q + 0),
@@ -679,7 +682,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         //     128 rows x 64 channels; rows M .. ceil32(M) - 1 get code 0) and
         //     its row scales
         const int m0 = tile_m * BM + wm * kWaveRows;
-        const int n0w = tile_n * BN + wn * (FW * 32);          // wave's first channel
+        const int n0w = tile_n * TBN + wn * (FW * 32);         // wave's first channel
         const int mpad = (M + 31) & ~31;
         if (tile_n == 0 && wn == 0 && lane < 32) {
 #pragma unroll
@@ -749,7 +752,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     constexpr int kStores = kWaveRows / kRowsPerStore;
     const int c = lane & (kRowChunks - 1);
     const int m0 = tile_m * BM + wm * kWaveRows;
-    const int n = tile_n * BN + wn * (FW * 32) + c * 8;
+    const int n = tile_n * TBN + wn * (FW * 32) + c * 8;
     uint4 out[kStores];
 #pragma unroll
     for (int i = 0; i < kStores; ++i) {
@@ -761,6 +764,39 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         const int r = i * kRowsPerStore + lane / kRowChunks;
         if (m0 + r < M && n < N) store_y16(Y + (size_t)(m0 + r) * N + n, out[i]);
     }
+}
+
+// Blocks [0, narrow_first) are BM x BN tiles of rows 0 .. tiles_m * BM - 1
+// in the XCD-aware order; blocks from narrow_first on (int containers, bf16
+// output) cover rows narrow_m0 .. M - 1 in tiles of BN / 2 channels.  A
+// ragged last round of a wide layer (a few rows past a whole number of
+// rounds) thus runs as twice as many half-width tiles, each about half as
+// long on these MFMA-bound formats, which the compute units pick up as the
+// full-width tiles of the previous round drain.  (An E2M3 tile is bound by
+// its operand stream, and a half-width one still reads the whole
+// activation panel: no gain there.)
+template <int FMT, int NS, bool ACC_OUT, int EPI>
+__global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
+    const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, const float* __restrict__ comp_a,
+    const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
+    int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, int narrow_first, int narrow_m0,
+    NextLayerQuant nx) {
+    if constexpr (EPI == kEpiBf16 && FMT != kFmtF6) {
+        if ((int)blockIdx.x >= narrow_first) {
+            const int t = (int)blockIdx.x - narrow_first;
+            const int rows = (M - narrow_m0 + BM - 1) / BM;       // narrow tile rows
+            gemm_tile<FMT, NS, ACC_OUT, EPI, BN / 2>(Xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                     comp_b, M, N, K, S, Y, acc_out,
+                                                     narrow_m0 / BM + t % rows, t / rows, nx);
+            return;
+        }
+    }
+    int tile_m, tile_n;
+    tile_of_block(blockIdx.x, narrow_first, tiles_m, tiles_n, tile_m, tile_n);
+    gemm_tile<FMT, NS, ACC_OUT, EPI, BN>(Xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N,
+                                         K, S, Y, acc_out, tile_m, tile_n, nx);
 }
 
 // ---------------------------------------------------------------------------
@@ -1047,12 +1083,14 @@ hipError_t launch_skinny(const uint8_t* xq, const float* row_scale, const uint8_
     return hipGetLastError();
 }
 
+// split_m > 0 (int containers, bf16 output): rows split_m .. M - 1 run as
+// narrow tiles in the same launch (see w4_gemm_kernel).
 template <int FMT, int NS, bool ACC_OUT, int EPI = kEpiBf16>
 hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                           const uint8_t* Wq, const float* w_scale, const float* comp_a,
                           const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                           int32_t* acc_out, hipStream_t stream,
-                          const NextLayerQuant& nx = NextLayerQuant{}) {
+                          const NextLayerQuant& nx = NextLayerQuant{}, int split_m = 0) {
     using C = Cfg<FMT, NS>;
     constexpr int kExtra = EPI != kEpiBf16 ? 1 : 0;
     static_assert(C::lds_bytes(1, kExtra) <= kLdsLimit, "LDS budget");
@@ -1063,12 +1101,18 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
         (const void*)w4_gemm_kernel<FMT, NS, ACC_OUT, EPI>,
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
-    const int tiles_m = (M + BM - 1) / BM;
     const int tiles_n = (N + BN - 1) / BN;
+    const bool split = EPI == kEpiBf16 && FMT != kFmtF6 && split_m > 0 && split_m < M &&
+                       split_m % BM == 0;
+    const int tiles_m = split ? split_m / BM : (M + BM - 1) / BM;
+    const int main_tiles = tiles_m * tiles_n;
+    const int narrow_tiles =
+        split ? ((M - split_m + BM - 1) / BM) * ((N + BN / 2 - 1) / (BN / 2)) : 0;
     hipLaunchKernelGGL((w4_gemm_kernel<FMT, NS, ACC_OUT, EPI>),
-                       dim3((unsigned)(tiles_m * tiles_n)), dim3(kThreads),
+                       dim3((unsigned)(main_tiles + narrow_tiles)), dim3(kThreads),
                        C::lds_bytes(S, kExtra), stream, xq, row_scale, sid, Wq, w_scale, comp_a,
-                       comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n, nx);
+                       comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n, main_tiles,
+                       split ? split_m : M, nx);
     return hipGetLastError();
 }
 
@@ -1110,12 +1154,13 @@ hipError_t launch_tiled(const uint8_t* xq, const float* row_scale, const uint8_t
                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                         int32_t* acc_out, hipStream_t stream,
-                        const NextLayerQuant& nx = NextLayerQuant{}) {
+                        const NextLayerQuant& nx = NextLayerQuant{}, int split_m = 0) {
     // every stream count fits a CU (calls with many streams may run one
     // workgroup per CU instead of two)
     static_assert(Cfg<FMT, kRing>::lds_bytes(RUDDER_MAX_STREAMS, 1) <= 160 * 1024, "LDS budget");
     return launch_variant<FMT, kRing, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                    comp_b, M, N, K, S, Y, acc_out, stream, nx);
+                                                    comp_b, M, N, K, S, Y, acc_out, stream, nx,
+                                                    split_m);
 }
 
 template <int FMT, bool ACC_OUT>
@@ -1134,7 +1179,8 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
     // streaming kernel reads the weights once per 128-row group, so this
     // pays only for narrow layers: groups * N <= kSplitMaxWidth (measured on
     // 2048-, 4096- and 8192-wide layers, where it saves 5-25%; on 12288- and
-    // 16384-wide layers the partial round is cheaper).
+    // 16384-wide layers the partial round is cheaper, and the int
+    // containers run it as half-width tiles).
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = ((M + BM - 1) / BM) * tiles_n;
     const int per_cu = (int)((160 * 1024) / Cfg<FMT, kRing>::lds_bytes(S));
@@ -1155,6 +1201,12 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
                 N, K, S, Y + (size_t)m_main * N,
                 ACC_OUT ? acc_out + (size_t)m_main * N : acc_out, stream);
         }
+        // wider layers, int containers: the remainder as half-width tiles in
+        // the same launch
+        if (FMT != kFmtF6 && m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && N >= BN)
+            return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
+                                              N, K, S, Y, acc_out, stream, NextLayerQuant{},
+                                              m_main);
     }
     return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
                                       S, Y, acc_out, stream);

@@ -25,8 +25,12 @@
 //     those go straight from global memory into registers, two stages ahead,
 //     and cost no LDS traffic.
 //   * Epilogue: dequantize + compensate in registers, stage the bf16 tile in
-//     LDS (XOR-swizzled 16-byte chunks), then store whole 512-byte row
-//     segments with 16-byte stores so every HBM line is written once.
+//     LDS (XOR-swizzled 16-byte chunks), then store it with 16-byte stores
+//     in whole 128-byte lines (64-byte halves for the narrow tiles below),
+//     so every HBM line is written once.
+//   * Ragged last round: a wide layer whose rows spill a little past a whole
+//     number of tile rounds (int containers) runs those rows as half-width
+//     tiles appended to the same launch.
 //   * E2M3 container (W4A4): 4-bit codes held as FP6 E2M3 feed
 //     v_mfma_scale_f32_32x32x64_f8f6f4 directly (unit scales): no widening, and
 //     twice the int8 rate.  Products of codes are small integers and every
@@ -744,10 +748,9 @@ __device__ __forceinline__ void gemm_tile(
         }
         return;
     }
-    // 2. whole-line stores of this wave's rows (its own LDS writes are
-    //    ordered before these reads)
-    //    All of the wave's staged rows are read back first (one LDS round
-    //    trip), then stored.
+    // 2. stores of this wave's rows (its own LDS writes are ordered before
+    //    these reads): all of its staged rows are read back first (one LDS
+    //    round trip), then stored, kRowChunks lanes per row.
     constexpr int kRowsPerStore = 64 / kRowChunks;
     constexpr int kStores = kWaveRows / kRowsPerStore;
     const int c = lane & (kRowChunks - 1);

@@ -66,10 +66,16 @@ KERNEL_SOURCES = ["w4a4_quantized_gemm_rudder_amd/csrc/w4_gemm.hip",
 
 
 def kernel_source_hash() -> str:
+    """Hash of the kernel sources' code: line comments and blank lines are
+    dropped, so a comment edit does not void counters taken on the same
+    kernels (the sources use no block comments)."""
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            for line in f:
+                code = line.split("//", 1)[0].rstrip()
+                if code:
+                    h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

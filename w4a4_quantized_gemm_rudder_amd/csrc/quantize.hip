@@ -192,35 +192,47 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
     __shared__ float s_delta[RUDDER_MAX_STREAMS];
     __shared__ float s_ia[RUDDER_MAX_STREAMS];
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int kblocks = K >> 6;
+    const int total = ((M + 31) >> 5) * kblocks;
+    const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool active = gw < total;
+    const int rb = gw / kblocks;
+    const int kb = gw - rb * kblocks;
+    const int r = rb * 32 + (lane & 31);
+    const int k0 = kb * 64 + 32 * (lane >> 5);
+
+    // The block's bf16 loads go out before the step-size table is built, so
+    // their latency overlaps it.
+    const bool row = active && r < M;
+    uint4 xv[4];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) xv[i] = make_uint4(0, 0, 0, 0);
+    if (row) {
+        s = sid[r] & (RUDDER_MAX_STREAMS - 1);
+        const uint4* xp = reinterpret_cast<const uint4*>(X + (size_t)r * K + k0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) xv[i] = xp[i];
+    }
     if (tid < RUDDER_MAX_STREAMS) {
         float d = tid < S ? delta[tid] : 0.0f;
         s_delta[tid] = d;
         s_ia[tid] = step_reciprocal(d);
     }
     __syncthreads();
-
-    const int lane = tid & 63;
-    const int kblocks = K >> 6;
-    const int total = ((M + 31) >> 5) * kblocks;
-    const int gw = blockIdx.x * (kThreads / 64) + __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (gw >= total) return;
-    const int rb = gw / kblocks;
-    const int kb = gw - rb * kblocks;
-    const int r = rb * 32 + (lane & 31);
-    const int k0 = kb * 64 + 32 * (lane >> 5);
+    if (!active) return;
 
     float c[32];
-    if (r < M) {
-        const int s = sid[r] & (RUDDER_MAX_STREAMS - 1);
+    if (row) {
         const float ia = s_ia[s];
-        const uint4* xp = reinterpret_cast<const uint4*>(X + (size_t)r * K + k0);
         // wave-uniform block: its 64 inverse smoothing factors through scalar
         // loads, each lane selecting its half
         const float* sb = inv_smooth + kb * 64;
         const bool upper = lane >= 32;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint4 x0 = xp[2 * h], x1 = xp[2 * h + 1];
+            const uint4 x0 = xv[2 * h], x1 = xv[2 * h + 1];
             const uint32_t xw[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
             float lo[16], hi[16], is[16];
             uniform_load16(sb + 16 * h, lo);

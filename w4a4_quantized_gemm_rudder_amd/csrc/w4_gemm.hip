@@ -769,9 +769,17 @@ __device__ __forceinline__ void gemm_tile(
     }
 }
 
-// Blocks [0, narrow_first) are BM x BN tiles of rows 0 .. tiles_m * BM - 1
-// in the XCD-aware order; blocks from narrow_first on (int containers, bf16
-// output) cover rows narrow_m0 .. M - 1 in tiles of BN / 2 channels.  A
+// The first touch_blocks blocks (a multiple of the XCD count, so the tile
+// blocks keep their XCD assignment) load one dword per 128-byte line of the
+// packed weights and exit.  The tiled kernel reads every weight panel from
+// several XCDs, many times over, and its weight stream is latency-bound;
+// with the weights cold in HBM (inside a model step each layer's weights
+// were last read a whole step earlier) these loads bring them into the
+// memory-side cache ahead of the tiles' own reads.
+// The other blocks, numbered from 0: [0, narrow_first) are BM x BN tiles of
+// rows 0 .. tiles_m * BM - 1 in the XCD-aware order; blocks from
+// narrow_first on (int containers, bf16 output) cover rows narrow_m0 .. M - 1
+// in tiles of BN / 2 channels.  A
 // ragged last round of a wide layer (a few rows past a whole number of
 // rounds) thus runs as twice as many half-width tiles, each about half as
 // long on these MFMA-bound formats, which the compute units pick up as the
@@ -785,10 +793,22 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
     int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, int narrow_first, int narrow_m0,
-    NextLayerQuant nx) {
+    int touch_blocks, NextLayerQuant nx) {
+    if ((int)blockIdx.x < touch_blocks) {
+        const size_t bytes = FMT == kFmtF6 ? (size_t)N * K * 3 / 4 : (size_t)N * K / 2;
+        const size_t lines = bytes / 128;
+        const uint32_t* p = reinterpret_cast<const uint32_t*>(Wq);
+        uint32_t v = 0;
+        for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < lines;
+             i += (size_t)touch_blocks * kThreads)
+            v ^= p[i * 32];
+        asm volatile("" ::"v"(v));          // the loads are the point; the data is not used
+        return;
+    }
+    const int bid = (int)blockIdx.x - touch_blocks;
     if constexpr (EPI == kEpiBf16 && FMT != kFmtF6) {
-        if ((int)blockIdx.x >= narrow_first) {
-            const int t = (int)blockIdx.x - narrow_first;
+        if (bid >= narrow_first) {
+            const int t = bid - narrow_first;
             const int rows = (M - narrow_m0 + BM - 1) / BM;       // narrow tile rows
             gemm_tile<FMT, NS, ACC_OUT, EPI, BN / 2>(Xq, row_scale, sid, Wq, w_scale, comp_a,
                                                      comp_b, M, N, K, S, Y, acc_out,
@@ -797,7 +817,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         }
     }
     int tile_m, tile_n;
-    tile_of_block(blockIdx.x, narrow_first, tiles_m, tiles_n, tile_m, tile_n);
+    tile_of_block(bid, narrow_first, tiles_m, tiles_n, tile_m, tile_n);
     gemm_tile<FMT, NS, ACC_OUT, EPI, BN>(Xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N,
                                          K, S, Y, acc_out, tile_m, tile_n, nx);
 }
@@ -817,6 +837,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyMaxM = 256;                 // rows handled by the small-M kernel
+constexpr int kTouchBlocks = 64;                 // weight touch blocks of a tiled launch
 constexpr int kSplitMaxWidth = 8192;             // see launch_fmt
 constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 
@@ -1111,11 +1132,14 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
     const int main_tiles = tiles_m * tiles_n;
     const int narrow_tiles =
         split ? ((M - split_m + BM - 1) / BM) * ((N + BN / 2 - 1) / (BN / 2)) : 0;
+    // weight touch blocks (few-row launches read the weights only once or
+    // twice and go without)
+    const int touch_blocks = M > kSkinnyMaxM ? kTouchBlocks : 0;
     hipLaunchKernelGGL((w4_gemm_kernel<FMT, NS, ACC_OUT, EPI>),
-                       dim3((unsigned)(main_tiles + narrow_tiles)), dim3(kThreads),
+                       dim3((unsigned)(touch_blocks + main_tiles + narrow_tiles)), dim3(kThreads),
                        C::lds_bytes(S, kExtra), stream, xq, row_scale, sid, Wq, w_scale, comp_a,
                        comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n, main_tiles,
-                       split ? split_m : M, nx);
+                       split ? split_m : M, touch_blocks, nx);
     return hipGetLastError();
 }
 
@@ -1217,51 +1241,11 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
 
 }  // namespace
 
-namespace {
-
-// One dword load per 128-byte line of a buffer, results unused: brings the
-// buffer into the memory-side cache shared by all XCDs.
-__global__ __launch_bounds__(256) void touch_lines_kernel(const uint32_t* __restrict__ p,
-                                                          size_t lines) {
-    uint32_t acc = 0;
-    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < lines;
-         i += (size_t)gridDim.x * 256)
-        acc ^= p[i * 32];
-    asm volatile("" ::"v"(acc));
-}
-
-hipError_t launch_touch(const uint8_t* p, size_t bytes, hipStream_t stream) {
-    const size_t lines = bytes / 128;      // whole lines (packed weights: K*N/2 or 3/4 K*N)
-    if (lines == 0) return hipSuccess;
-    const size_t want = (lines + 255) / 256;
-    const unsigned blocks = (unsigned)(want < 2048 ? want : 2048);
-    hipLaunchKernelGGL(touch_lines_kernel, dim3(blocks), dim3(256), 0, stream,
-                       reinterpret_cast<const uint32_t*>(p), lines);
-    return hipGetLastError();
-}
-
-// The tiled kernel reads every weight panel from several XCDs, many times
-// over; with the panels cold in HBM (the case inside a model step, where
-// each layer's weights were last read a whole step earlier) its weight
-// stream waits on HBM latency.  A line-touch pass first puts the packed
-// weights in the memory-side cache: ~3 us for 12.6 MB, against 4-16 us
-// saved on a cold 8384-row call.  Few-row calls read the weights once and
-// skip it.
-hipError_t touch_weights(const uint8_t* Wq, int M, int N, int K, int codes, hipStream_t stream) {
-    if (M <= kSkinnyMaxM) return hipSuccess;
-    const size_t bytes = codes == RUDDER_CODES_E2M3 ? (size_t)N * K * 3 / 4 : (size_t)N * K / 2;
-    return launch_touch(Wq, bytes, stream);
-}
-
-}  // namespace
-
 hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* sid,
                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
                          const float* comp_b, int M, int N, int K, int S, int abits, int codes,
                          uint16_t* Y, int32_t* acc_out, hipStream_t stream) {
     const uint8_t* xq = static_cast<const uint8_t*>(Xq);
-    const hipError_t te = touch_weights(Wq, M, N, K, codes, stream);
-    if (te != hipSuccess) return te;
 #define RUDDER_LAUNCH(FMT)                                                                   \
     return acc_out ? launch_fmt<FMT, true>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, \
                                            N, K, S, Y, acc_out, stream)                       \
@@ -1320,9 +1304,6 @@ hipError_t launch_linear_gelu_quant(const void* Xq, const float* row_scale, cons
                                     const uint8_t* Wq, const float* w_scale, const float* comp_a,
                                     const float* comp_b, int M, int N, int K, int S, int abits,
                                     int codes, const NextLayerQuant& next, hipStream_t stream) {
-    // No line-touch pass here: measured on the up -> down chain run back to
-    // back, whose weights stay cache-resident between calls, it only adds
-    // its own time.
     const uint8_t* xq = static_cast<const uint8_t*>(Xq);
     if (codes == RUDDER_CODES_E2M3)
         return launch_fused_fmt<kFmtF6>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,

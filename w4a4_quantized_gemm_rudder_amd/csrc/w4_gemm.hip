@@ -31,6 +31,9 @@
 //   * Ragged last round: a wide layer whose rows spill a little past a whole
 //     number of tile rounds (int containers) runs those rows as half-width
 //     tiles appended to the same launch.
+//   * Weight touch: a few leading blocks of each launch read the packed
+//     weights once, line by line, so that the tiles' many re-reads of them
+//     hit the memory-side cache instead of HBM.
 //   * E2M3 container (W4A4): 4-bit codes held as FP6 E2M3 feed
 //     v_mfma_scale_f32_32x32x64_f8f6f4 directly (unit scales): no widening, and
 //     twice the int8 rate.  Products of codes are small integers and every

@@ -16,7 +16,9 @@ seeded synthetic tensors already resident in HBM.
 Prints ONE JSON line.  `value` is whole-step throughput in TOPS (2*M*N*K
 summed over the four linears, per second, both kernels of each linear
 included); `us_per_step` is the latency of one step, timed over K steps with
-nothing but the step's launches on the stream.  The same K steps then run
+nothing but the step's launches on the stream, after W untimed steps (the
+default W, ~40 ms of steps, lets the clocks settle to their steady state
+under sustained load, as in a running denoising loop).  The same K steps then run
 again with a HIP event pair around every GEMM launch on the launch stream
 (`us_per_step_with_kernel_events`: the records add gaps between launches);
 those events give `gemm_kernels` and `roofline`, which describes the kernel
@@ -83,7 +85,10 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=32)
-    p.add_argument("--warmup", type=int, default=5)
+    # ~40 ms of steps: the part's clocks reach their steady state under
+    # sustained load only after some tens of milliseconds (5 warmup steps:
+    # ~412 us per step, 100 or 300: ~370)
+    p.add_argument("--warmup", type=int, default=100)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--w4a4-codes", choices=["int", "e2m3"], default="e2m3",

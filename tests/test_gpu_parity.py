@@ -160,12 +160,13 @@ def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
 # Wider layers with the int containers: the rows past the last whole round
 # run as half-width (128-channel) tiles in the same launch.  8192 + 192 rows
 # x 6144 channels = 1584 tiles of 128 x 256 for 512 resident workgroups;
-# 8192 + 100 rows x 12288 channels; one and two k-stages.  Every row is
-# compared.
+# 8192 + 100 rows x 12288 channels; 8128 channels, whose last half-width
+# tile is half past N; one and two k-stages.  Every row is compared.
 @pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes", [
     (8384, 128, 6144, 3, 8, False, 44, CODES_INT),
     (8384, 256, 6144, 3, 4, True, 45, CODES_INT),
     (8292, 128, 12288, 4, 8, False, 46, CODES_INT),
+    (8384, 128, 8128, 3, 8, False, 47, CODES_INT),      # last narrow tile half outside N
 ])
 def test_round_remainder_narrow_tiles(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case narrow tail M={M} K={K} N={N} S={S} abits={abits} codes={codes}")

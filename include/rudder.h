@@ -193,11 +193,10 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
  *   Y          out: bf16 bits [M][N], row-major
  *   acc_out    optional out: int32 [M][N] row-major raw accumulators
  *              sum_k qa*qw (a verification aid; pass NULL on the hot path)
- * Launches: for M > 256 the tiled GEMM (its first blocks read the packed
- * weights once more, so that they are cache-resident for the tiles'
- * repeated reads), and for some row counts a second kernel for the last
- * rows; for M <= 256 one weight-streaming kernel.  All on `stream`, in
- * order.
+ * Launches: for M > 256 one tiled GEMM launch (its first blocks read the
+ * packed weights once more, so that they are cache-resident for the tiles'
+ * repeated reads; for some row counts its last blocks take the last rows in
+ * narrower pieces); for M <= 256 one weight-streaming kernel.  On `stream`.
  * Errors: INVALID_ARG for a null required pointer, M < 0, N or K <= 0,
  * N % 32 != 0, S outside 1..8, abits not 4 or 8, an unknown container or
  * E2M3 with abits = 8, Xq/Wq/w_scale/comp_a/comp_b/Y/acc_out not 16-byte

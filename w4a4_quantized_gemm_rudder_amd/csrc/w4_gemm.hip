@@ -28,9 +28,10 @@
 //     LDS (XOR-swizzled 16-byte chunks), then store it with 16-byte stores
 //     in whole 128-byte lines (64-byte halves for the narrow tiles below),
 //     so every HBM line is written once.
-//   * Ragged last round: a wide layer whose rows spill a little past a whole
-//     number of tile rounds (int containers) runs those rows as half-width
-//     tiles appended to the same launch.
+//   * Ragged last round: when the rows spill a little past a whole number of
+//     tile rounds, those rows run in the same launch, after the tiles: as
+//     weight-streaming blocks for narrow layers, as half-width tiles for
+//     wider ones (int containers).
 //   * Weight touch: a few leading blocks of each launch read the packed
 //     weights once, line by line, so that the tiles' many re-reads of them
 //     hit the memory-side cache instead of HBM.
@@ -772,6 +773,14 @@ __device__ __forceinline__ void gemm_tile(
     }
 }
 
+template <int FMT, int FA, int NW, bool ACC_OUT, int SW>
+__device__ __forceinline__ void skinny_tile(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
+    const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, const float* __restrict__ comp_a,
+    const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
+    int32_t* __restrict__ acc_out, int cb, int rg, uint8_t* smem);
+
 // The first touch_blocks blocks (a multiple of the XCD count, so the tile
 // blocks keep their XCD assignment) load one dword per 128-byte line of the
 // packed weights and exit.  The tiled kernel reads every weight panel from
@@ -782,7 +791,11 @@ __device__ __forceinline__ void gemm_tile(
 // The other blocks, numbered from 0: [0, narrow_first) are BM x BN tiles of
 // rows 0 .. tiles_m * BM - 1 in the XCD-aware order; blocks from
 // narrow_first on (int containers, bf16 output) cover rows narrow_m0 .. M - 1
-// in tiles of BN / 2 channels.  A
+// in tiles of BN / 2 channels; blocks from tail_first on (bf16 output)
+// cover rows tail_m0 .. M - 1 of a narrow layer as streaming blocks of 64
+// rows x 32 channels (the weight-streaming kernel's work, four waves
+// splitting k), which the compute units pick up as the last round of tiles
+// drains.  A
 // ragged last round of a wide layer (a few rows past a whole number of
 // rounds) thus runs as twice as many half-width tiles, each about half as
 // long on these MFMA-bound formats, which the compute units pick up as the
@@ -796,7 +809,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
     int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, int narrow_first, int narrow_m0,
-    int touch_blocks, NextLayerQuant nx) {
+    int touch_blocks, int tail_first, int tail_m0, NextLayerQuant nx) {
     if ((int)blockIdx.x < touch_blocks) {
         const size_t bytes = FMT == kFmtF6 ? (size_t)N * K * 3 / 4 : (size_t)N * K / 2;
         const size_t lines = bytes / 128;
@@ -809,6 +822,20 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         return;
     }
     const int bid = (int)blockIdx.x - touch_blocks;
+    if constexpr (EPI == kEpiBf16) {
+        if (bid >= tail_first) {
+            extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+            using F = Fmt<FMT>;
+            const int t = bid - tail_first;
+            const int cbs = N / 32;
+            const size_t a_off = (size_t)(tail_m0 / 32) * (K / F::kKSub) * F::kABlock;
+            skinny_tile<FMT, 2, 1, ACC_OUT, kWaves>(
+                Xq + a_off, row_scale + tail_m0, sid + tail_m0, Wq, w_scale, comp_a, comp_b,
+                M - tail_m0, N, K, S, Y + (size_t)tail_m0 * N,
+                ACC_OUT ? acc_out + (size_t)tail_m0 * N : acc_out, t % cbs, t / cbs, lds);
+            return;
+        }
+    }
     if constexpr (EPI == kEpiBf16 && FMT != kFmtF6) {
         if (bid >= narrow_first) {
             const int t = bid - narrow_first;
@@ -926,36 +953,51 @@ struct SkinnyChunk {
                                      : (kFit >= 8 ? 8 : kFit >= 4 ? 4 : kFit >= 2 ? 2 : 1);
 };
 
-template <int FMT, int FA, int NW, bool ACC_OUT>
-__global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
+// LDS of one streaming block: the sum tile (exact integer dot products,
+// summed as int32; fp32 partials of the E2M3 path are integers below 2^24
+// and convert exactly), the epilogue operands w_scale[NC], comp_a[S][NC],
+// comp_b[S][NC], and the rows' scales and streams.
+template <int FA, int NW>
+struct SkinnySmem {
+    static constexpr int NC = NW * 32;               // channels of the block
+    static constexpr int kPitch = NC + 1;            // row pitch (words) of the sum tile
+    static constexpr int kTabMax = NC * (1 + 2 * RUDDER_MAX_STREAMS);
+    static constexpr int kSumBytes = FA * 32 * kPitch * 4;
+    static constexpr int kTabBytes = kTabMax * 4;
+    static constexpr int kBytes = kSumBytes + kTabBytes + 2 * FA * 32 * 4;
+};
+
+// One streaming block (SW waves): channel block cb (NW * 32 channels) and
+// row group rg (FA * 32 rows); smem holds SkinnySmem<FA, NW>::kBytes of LDS.
+template <int FMT, int FA, int NW, bool ACC_OUT, int SW>
+__device__ __forceinline__ void skinny_tile(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
     const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
-    int32_t* __restrict__ acc_out) {
+    int32_t* __restrict__ acc_out, int cb, int rg, uint8_t* smem) {
     using F = Fmt<FMT>;
     using Acc = typename F::Acc;
-    constexpr int NC = NW * 32;                    // channels of this workgroup
-    constexpr int kPitch = NC + 1;                 // LDS row pitch (words) of the sum tile
-    constexpr int kTabMax = NC * (1 + 2 * RUDDER_MAX_STREAMS);
-    constexpr int kTabPer = (kTabMax + kSkinnyThreads - 1) / kSkinnyThreads;
-    static_assert(FA * 32 <= kSkinnyThreads, "one thread per row for the row data");
-    // exact integer dot products, summed as int32 (fp32 partials of the
-    // E2M3 path are integers below 2^24 and convert exactly)
-    __shared__ int sum[FA * 32 * kPitch];
-    // per-block epilogue operands: w_scale[NC], comp_a[S][NC], comp_b[S][NC]
-    __shared__ float tab[kTabMax];
-    __shared__ float rows_rs[FA * 32];
-    __shared__ int rows_s[FA * 32];
+    using L = SkinnySmem<FA, NW>;
+    constexpr int kThr = 64 * SW;
+    constexpr int NC = L::NC;
+    constexpr int kPitch = L::kPitch;
+    constexpr int kTabMax = L::kTabMax;
+    constexpr int kTabPer = (kTabMax + kThr - 1) / kThr;
+    static_assert(FA * 32 <= kThr, "one thread per row for the row data");
+    int* sum = reinterpret_cast<int*>(smem);
+    float* tab = reinterpret_cast<float*>(smem + L::kSumBytes);
+    float* rows_rs = reinterpret_cast<float*>(smem + L::kSumBytes + L::kTabBytes);
+    int* rows_s = reinterpret_cast<int*>(smem + L::kSumBytes + L::kTabBytes + FA * 32 * 4);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
-    const int nb0 = blockIdx.x * NW;               // first 32-channel block
+    const int nb0 = cb * NW;                       // first 32-channel block
     const int kblocks = K / F::kKSub;
-    // this workgroup's rows: group blockIdx.y of FA * 32 rows
+    // this block's rows: group rg of FA * 32 rows
     {
-        const int row0 = blockIdx.y * FA * 32;
+        const int row0 = rg * FA * 32;
         Xq += (size_t)(row0 >> 5) * kblocks * F::kABlock;
         row_scale += row0;
         sid += row0;
@@ -965,7 +1007,7 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
     }
     const int mb = (M + 31) >> 5;                  // 32-row blocks present (<= FA)
 
-    for (int i = tid; i < FA * 32 * kPitch; i += kSkinnyThreads) sum[i] = 0;
+    for (int i = tid; i < FA * 32 * kPitch; i += kThr) sum[i] = 0;
 
     // epilogue operands: fetched now (in flight with the k loop), written to
     // LDS after it
@@ -980,7 +1022,7 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
     float e_tab[kTabPer];
 #pragma unroll
     for (int t = 0; t < kTabPer; ++t) {
-        const int i = tid + t * kSkinnyThreads;
+        const int i = tid + t * kThr;
         e_tab[t] = i < ntab ? *tab_src(i) : 0.0f;
     }
     const float e_rs = tid < M ? row_scale[tid] : 0.0f;
@@ -998,7 +1040,7 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
     // of D substeps; the loads of chunk c+1 are issued before the MFMAs of
     // chunk c, so two chunks (the whole range for short K) are in flight.
     constexpr int D = SkinnyChunk<FMT, FA, NW>::D;
-    const int per_wave = (kblocks + kSkinnyWaves - 1) / kSkinnyWaves;
+    const int per_wave = (kblocks + SW - 1) / SW;
     const int j0 = wave * per_wave;
     const int j1 = min(j0 + per_wave, kblocks);
     SkinnyOps<FMT, FA, NW> ops[2][D];
@@ -1024,7 +1066,7 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
     }
 #pragma unroll
     for (int t = 0; t < kTabPer; ++t) {
-        const int i = tid + t * kSkinnyThreads;
+        const int i = tid + t * kThr;
         if (i < ntab) tab[i] = e_tab[t];
     }
     if (tid < FA * 32) {
@@ -1052,7 +1094,7 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
 
     // epilogue: item = (row m, 8-channel group c); NC / 8 items per row
     constexpr int kGroups = NC / 8;
-    for (int item = tid; item < mb * 32 * kGroups; item += kSkinnyThreads) {
+    for (int item = tid; item < mb * 32 * kGroups; item += kThr) {
         const int m = item / kGroups;
         const int c = item % kGroups;
         if (m >= M) continue;
@@ -1086,6 +1128,19 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
         }
     }
 }
+
+template <int FMT, int FA, int NW, bool ACC_OUT>
+__global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
+    const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,
+    const uint8_t* __restrict__ sid, const uint8_t* __restrict__ Wq,
+    const float* __restrict__ w_scale, const float* __restrict__ comp_a,
+    const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
+    int32_t* __restrict__ acc_out) {
+    __shared__ __attribute__((aligned(16))) uint8_t smem[SkinnySmem<FA, NW>::kBytes];
+    skinny_tile<FMT, FA, NW, ACC_OUT, kSkinnyWaves>(Xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                    comp_b, M, N, K, S, Y, acc_out, blockIdx.x,
+                                                    blockIdx.y, smem);
+}
 int device_cus();
 
 // NW = 2 (64 channels per workgroup) halves the activation re-reads, which
@@ -1111,14 +1166,18 @@ hipError_t launch_skinny(const uint8_t* xq, const float* row_scale, const uint8_
 }
 
 // split_m > 0 (int containers, bf16 output): rows split_m .. M - 1 run as
-// narrow tiles in the same launch (see w4_gemm_kernel).
+// narrow tiles in the same launch; tail_m0 > 0 (bf16 output): rows
+// tail_m0 .. M - 1 run as streaming blocks in the same launch (see
+// w4_gemm_kernel).
 template <int FMT, int NS, bool ACC_OUT, int EPI = kEpiBf16>
 hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                           const uint8_t* Wq, const float* w_scale, const float* comp_a,
                           const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                           int32_t* acc_out, hipStream_t stream,
-                          const NextLayerQuant& nx = NextLayerQuant{}, int split_m = 0) {
+                          const NextLayerQuant& nx = NextLayerQuant{}, int split_m = 0,
+                          int tail_m0 = 0) {
     using C = Cfg<FMT, NS>;
+    static_assert(SkinnySmem<2, 1>::kBytes <= C::lds_bytes(1), "streaming blocks' LDS");
     constexpr int kExtra = EPI != kEpiBf16 ? 1 : 0;
     static_assert(C::lds_bytes(1, kExtra) <= kLdsLimit, "LDS budget");
     static_assert(EPI == kEpiBf16 || Waves<FMT>::FW == 2, "code epilogue: 64 channels per wave");
@@ -1131,18 +1190,23 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
     const int tiles_n = (N + BN - 1) / BN;
     const bool split = EPI == kEpiBf16 && FMT != kFmtF6 && split_m > 0 && split_m < M &&
                        split_m % BM == 0;
-    const int tiles_m = split ? split_m / BM : (M + BM - 1) / BM;
+    const bool tail = EPI == kEpiBf16 && !split && tail_m0 > 0 && tail_m0 < M &&
+                      tail_m0 % BM == 0 && M - tail_m0 <= kSkinnyMaxM;
+    const int tiles_m = split ? split_m / BM : (tail ? tail_m0 / BM : (M + BM - 1) / BM);
     const int main_tiles = tiles_m * tiles_n;
     const int narrow_tiles =
         split ? ((M - split_m + BM - 1) / BM) * ((N + BN / 2 - 1) / (BN / 2)) : 0;
+    const int tail_blocks = tail ? ((M - tail_m0 + 63) / 64) * (N / 32) : 0;
     // weight touch blocks (few-row launches read the weights only once or
     // twice and go without)
     const int touch_blocks = M > kSkinnyMaxM ? kTouchBlocks : 0;
     hipLaunchKernelGGL((w4_gemm_kernel<FMT, NS, ACC_OUT, EPI>),
-                       dim3((unsigned)(touch_blocks + main_tiles + narrow_tiles)), dim3(kThreads),
+                       dim3((unsigned)(touch_blocks + main_tiles + narrow_tiles + tail_blocks)),
+                       dim3(kThreads),
                        C::lds_bytes(S, kExtra), stream, xq, row_scale, sid, Wq, w_scale, comp_a,
                        comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n, main_tiles,
-                       split ? split_m : M, touch_blocks, nx);
+                       split ? split_m : M, touch_blocks,
+                       tail ? main_tiles + narrow_tiles : 0x7FFFFFFF, tail ? tail_m0 : M, nx);
     return hipGetLastError();
 }
 
@@ -1184,13 +1248,14 @@ hipError_t launch_tiled(const uint8_t* xq, const float* row_scale, const uint8_t
                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                         int32_t* acc_out, hipStream_t stream,
-                        const NextLayerQuant& nx = NextLayerQuant{}, int split_m = 0) {
+                        const NextLayerQuant& nx = NextLayerQuant{}, int split_m = 0,
+                        int tail_m0 = 0) {
     // every stream count fits a CU (calls with many streams may run one
     // workgroup per CU instead of two)
     static_assert(Cfg<FMT, kRing>::lds_bytes(RUDDER_MAX_STREAMS, 1) <= 160 * 1024, "LDS budget");
     return launch_variant<FMT, kRing, ACC_OUT, EPI>(xq, row_scale, sid, Wq, w_scale, comp_a,
                                                     comp_b, M, N, K, S, Y, acc_out, stream, nx,
-                                                    split_m);
+                                                    split_m, tail_m0);
 }
 
 template <int FMT, bool ACC_OUT>
@@ -1203,13 +1268,14 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
         return launch_small<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N,
                                           K, S, Y, acc_out, stream);
     // Ragged last round: when the tiles fill whole rounds of resident
-    // workgroups except for a few rows (at most kSkinnyMaxM), the tiled
-    // kernel takes the rows of the full rounds and the weight-streaming
-    // kernel the rest, instead of a nearly empty extra round of tiles.  The
-    // streaming kernel reads the weights once per 128-row group, so this
-    // pays only for narrow layers: groups * N <= kSplitMaxWidth (measured on
-    // 2048-, 4096- and 8192-wide layers, where it saves 5-25%; on 12288- and
-    // 16384-wide layers the partial round is cheaper, and the int
+    // workgroups except for a few rows (at most kSkinnyMaxM), the tiles take
+    // the rows of the full rounds and weight-streaming blocks appended to
+    // the same launch take the rest, instead of a nearly empty extra round
+    // of tiles; those blocks start as the tiles drain, with no launch gap.
+    // Streaming reads the weights once per row group, so this pays only for
+    // narrow layers: groups * N <= kSplitMaxWidth (measured on 2048-, 4096-
+    // and 8192-wide layers, where a separate streaming launch saved 5-25%; on
+    // 12288- and 16384-wide layers the partial round is cheaper, and the int
     // containers run it as half-width tiles).
     const int tiles_n = (N + BN - 1) / BN;
     const int tiles = ((M + BM - 1) / BM) * tiles_n;
@@ -1220,17 +1286,10 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
         const int m_main = (full * slots / tiles_n) * BM;
         const int tail = M - m_main;
         const int groups = (tail + 127) / 128;
-        if (m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && groups * N <= kSplitMaxWidth) {
-            const hipError_t e = launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale,
-                                                            comp_a, comp_b, m_main, N, K, S, Y,
-                                                            acc_out, stream);
-            if (e != hipSuccess) return e;
-            const size_t a_off = (size_t)(m_main / 32) * (K / Fmt<FMT>::kKSub) * Fmt<FMT>::kABlock;
-            return launch_small<FMT, ACC_OUT>(
-                xq + a_off, row_scale + m_main, sid + m_main, Wq, w_scale, comp_a, comp_b, tail,
-                N, K, S, Y + (size_t)m_main * N,
-                ACC_OUT ? acc_out + (size_t)m_main * N : acc_out, stream);
-        }
+        if (m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && groups * N <= kSplitMaxWidth)
+            return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
+                                              N, K, S, Y, acc_out, stream, NextLayerQuant{}, 0,
+                                              m_main);
         // wider layers, int containers: the remainder as half-width tiles in
         // the same launch
         if (FMT != kFmtF6 && m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && N >= BN)

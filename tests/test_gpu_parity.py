@@ -142,15 +142,17 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     log(f"  {_random_layer_case(M, K, N, S, abits, dynamic, seed, codes)}")
 
 
-# Row counts just past a whole number of tile rounds: the tiled kernel takes
-# the rows of the full rounds and the weight-streaming kernel the remainder
-# (8192 + 100 rows x 2048 channels = 520 tiles of 128 x 256 for 512 resident
-# workgroups).  Every row is compared.
+# Row counts just past a whole number of tile rounds: the tiles take the rows
+# of the full rounds and weight-streaming blocks in the same launch the
+# remainder (8192 + 100 rows x 2048 channels = 520 tiles of 128 x 256 for 512
+# resident workgroups).  Every row is compared.
 @pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes", [
     (8292, 128, 2048, 3, 8, False, 40, CODES_INT),
     (8292, 256, 2048, 3, 4, True, 41, CODES_E2M3),
     (8292, 128, 2048, 2, 4, False, 42, CODES_INT),
     (8384, 256, 2048, 3, 4, False, 43, CODES_E2M3),     # 192-row remainder
+    (8384, 512, 4096, 3, 8, True, 48, CODES_INT),       # two full rounds, 4096 wide
+    (8292, 384, 4096, 4, 4, False, 49, CODES_E2M3),
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")

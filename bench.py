@@ -38,6 +38,9 @@ same form, steps cycling through its step-indexed scale sets).
 the 4-bit codes held as FP6 E2M3 for the f8f6f4 matrix cores, fp32
 accumulation, exact for integer codes) or "int" (int4 codes widened to int8
 for the int8 matrix cores).  Outputs are identical either way.
+--w4a8-codes does the same for the W4A8 linears: "int" (int8 codes, int8
+matrix cores) or "e2m3" (each int8 code as two E2M3 digit planes, two f8f6f4
+MFMAs per product).
 Comparators (context only): torch.matmul in bf16 and torch._int_mm (hipBLASLt
 int8 GEMM, no quantization or epilogue) on the same shapes.
 """
@@ -93,6 +96,8 @@ def parse_args():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--w4a4-codes", choices=["int", "e2m3"], default="e2m3",
                    help="code container of the W4A4 linears (identical outputs)")
+    p.add_argument("--w4a8-codes", choices=["int", "e2m3"], default="int",
+                   help="code container of the W4A8 linears (identical outputs)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-small-m", action="store_true",
                    help="skip the few-row (weight-streaming) calls")
@@ -122,7 +127,8 @@ def _to_dev(a, torch):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def prepare(wl_name: str, seed: int, torch, rudder, W, w4a4_codes: str = "int"):
+def prepare(wl_name: str, seed: int, torch, rudder, W, w4a4_codes: str = "int",
+            w4a8_codes: str = "int"):
     wi = W.make_inputs(wl_name, seed=seed)
     wl = wi.workload
     S = wl.S
@@ -138,7 +144,8 @@ def prepare(wl_name: str, seed: int, torch, rudder, W, w4a4_codes: str = "int"):
         Wd = _to_dev_bf16(L.w, torch)
         s_d = _to_dev(L.smooth, torch)
         abits = L.layer.abits
-        codes = rudder.CODES_E2M3 if (abits == 4 and w4a4_codes == "e2m3") else rudder.CODES_INT
+        e2m3 = (w4a4_codes if abits == 4 else w4a8_codes) == "e2m3"
+        codes = rudder.CODES_E2M3 if e2m3 else rudder.CODES_INT
         Wq, ws, inv = rudder.quantize_weights(Wd, s_d, codes)
         K, N = L.layer.K, L.layer.N
         if L.act_scale is not None:
@@ -496,7 +503,8 @@ def main():
     rudder.load_library()
     torch.cuda.set_device(0)
 
-    wi, sid_d, layers = prepare(args.workload, args.seed, torch, rudder, W, args.w4a4_codes)
+    wi, sid_d, layers = prepare(args.workload, args.seed, torch, rudder, W, args.w4a4_codes,
+                                args.w4a8_codes)
     wl = wi.workload
     torch.cuda.synchronize()
 
@@ -557,8 +565,12 @@ def main():
     avg_ms = float(np.mean(gemm_ms[dominant]))
     ops_per_launch = float(np.mean(gemm_ops[dominant]))
     achieved = ops_per_launch / (avg_ms * 1e-3) / 1e12
-    # a contraction is priced against the peak of the matrix-core type it runs on
-    dom_peak = FP6_PEAK_TFLOPS if "e2m3" in dominant else INT8_PEAK_TOPS
+    # a contraction is priced against the peak of the matrix-core type it runs
+    # on; 8-bit codes in the E2M3 container take two FP6 MFMAs per product
+    if "e2m3" not in dominant:
+        dom_peak = INT8_PEAK_TOPS
+    else:
+        dom_peak = FP6_PEAK_TFLOPS / (2 if dominant.startswith("w4a8") else 1)
     per_kernel = {k: {"avg_launch_us": round(float(np.mean(v)) * 1e3, 2),
                       "launches_per_step": len(v) // args.steps,
                       "tops": round(float(np.mean(gemm_ops[k])) / (float(np.mean(v)) * 1e-3)

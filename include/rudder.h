@@ -74,6 +74,23 @@
  * bit string (code t in bits 6t..6t+5).  Bits 0..127 of slot l are stored at
  * byte 16*l of the block (plane 0, 1024 bytes) and bits 128..191 at byte
  * 1024 + 8*l (plane 1, 512 bytes).  Padding rows hold code 0.
+ *
+ * E2M3 container for 8-bit activation codes (abits = 8, "codes" =
+ * RUDDER_CODES_E2M3; the weights of such a layer use the E2M3 container
+ * above).  Each code q in [-127, 127] is split into two digits,
+ * q = 16 h + l with l = ((q + 8) mod 16) - 8 in [-8, 7] and
+ * h = (q - l) / 16 in [-8, 8], and the digits are held as the E2M3 values
+ * h / 2 and l / 2 (multiples of 1/2 with magnitude at most 4, all exact in
+ * E2M3; the field of a value v is its standard E2M3 encoding:
+ * |v| = m / 8 with exponent field 0, or (1 + m / 8) * 2^(e - 1) with
+ * exponent field e = 1..3, mantissa field m, bit 5 the sign, +0 as 0x00).
+ * The matrix is cut into 32 x 64 blocks of 3072 bytes at block index
+ * rb * (K/64) + kb: bytes 0..1535 hold the h / 2 values of the block and
+ * bytes 1536..3071 the l / 2 values, each half laid out as a 1536-byte block
+ * above.  The matrix cores multiply each half with the weight codes under
+ * E8M0 block scales 2^5 and 2^1, so the fp32 accumulator holds sum q * w
+ * exactly while |sum| < 2^24, which 127 * 7 * K guarantees for
+ * K <= RUDDER_MAX_K_E2M3_A8.  Padding rows hold code 0.
  * ---------------------------------------------------------------------------
  */
 #ifndef RUDDER_H
@@ -96,11 +113,13 @@ typedef enum {
 /* Code containers of the packed weight and activation codes. */
 typedef enum {
     RUDDER_CODES_INT = 0,   /* int4 split-nibble words / int8 bytes; int8 matrix cores */
-    RUDDER_CODES_E2M3 = 1   /* 4-bit codes held as FP6 E2M3 (W4A4 only); f8f6f4 matrix cores */
+    RUDDER_CODES_E2M3 = 1   /* codes held as FP6 E2M3 (8-bit activation codes as two
+                               digit planes); f8f6f4 matrix cores */
 } rudder_codes_t;
 
 #define RUDDER_MAX_STREAMS 8      /* S, the number of token streams, is 1..8 */
 #define RUDDER_MAX_K 65536        /* keeps every scaled int32 accumulator exact */
+#define RUDDER_MAX_K_E2M3_A8 16384 /* keeps the fp32 sums of 8-bit E2M3 codes exact */
 
 /* Bytes of packed weight codes for a K x N layer: N * K / 2 (RUDDER_CODES_INT;
  * K, N multiples of 32) or N * K * 3 / 4 (RUDDER_CODES_E2M3; K a multiple of
@@ -109,7 +128,9 @@ size_t rudder_packed_weight_bytes(int K, int N, int codes);
 
 /* Bytes of activation codes for M rows (rounded up to 32) of K channels:
  * ceil(M/32)*32 * K * abits / 8 (RUDDER_CODES_INT), or ceil(M/32)*32 * K * 3/4
- * (RUDDER_CODES_E2M3, abits = 4, K a multiple of 64).  0 for invalid sizes. */
+ * (RUDDER_CODES_E2M3, abits = 4) or ceil(M/32)*32 * K * 3/2
+ * (RUDDER_CODES_E2M3, abits = 8), K a multiple of 64 for E2M3.  0 for invalid
+ * sizes. */
 size_t rudder_packed_act_bytes(int M, int K, int abits, int codes);
 
 /* Bytes of device workspace rudder_quant_act needs in dynamic mode. */
@@ -123,8 +144,8 @@ size_t rudder_quant_act_workspace_bytes(int S);
  *   W          bf16 bits [K][N], row-major (input channel k, output channel n)
  *   smooth     fp32 [K], s[k] > 0
  *   K, N       > 0, multiples of 32 (K a multiple of 64 for RUDDER_CODES_E2M3)
- *   codes      container of Wq: RUDDER_CODES_INT (any layer) or
- *              RUDDER_CODES_E2M3 (only for W4A4 layers run with that container)
+ *   codes      container of Wq: RUDDER_CODES_INT or RUDDER_CODES_E2M3, the
+ *              container the layer's activations use
  *   Wq         out: rudder_packed_weight_bytes(K, N, codes) bytes, MFMA-tiled
  *              layout with R = N (row = output channel)
  *   w_scale    out: fp32 [N]
@@ -156,16 +177,16 @@ rudder_status_t rudder_quantize_weights(const uint16_t* W, const float* smooth, 
  *              device scratch; ignored (may be NULL) in static mode
  *   M >= 0 (M = 0 is a no-op), K > 0 multiple of 32, 1 <= S <= 8,
  *   abits in {4, 8}
- *   codes      container of Xq: RUDDER_CODES_INT, or RUDDER_CODES_E2M3 (abits
- *              = 4, K a multiple of 64)
+ *   codes      container of Xq: RUDDER_CODES_INT, or RUDDER_CODES_E2M3 (K a
+ *              multiple of 64)
  *   Xq         out: rudder_packed_act_bytes(M, K, abits, codes) bytes,
  *              MFMA-tiled layout with R = M; padding rows are 0
  *   row_scale  out: fp32 [M], row_scale[m] = D[stream_id[m]]
  * Errors: INVALID_ARG for null X/stream_id/inv_smooth/Xq/row_scale, a null
  * workspace in dynamic mode, M < 0, K <= 0, K % 32 != 0, S outside 1..8,
- * abits not 4 or 8, an unknown container or E2M3 with abits = 8 or
- * K % 64 != 0, X/inv_smooth/Xq/workspace not 16-byte aligned;
- * UNSUPPORTED for K > RUDDER_MAX_K.
+ * abits not 4 or 8, an unknown container or E2M3 with K % 64 != 0,
+ * X/inv_smooth/Xq/workspace not 16-byte aligned; UNSUPPORTED for
+ * K > RUDDER_MAX_K.
  * Dynamic mode enqueues three kernels (partial absmax, finalize, quantize);
  * static mode one.
  */
@@ -183,9 +204,10 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
  *   Xq, row_scale, stream_id   from rudder_quant_act (same M, K, abits, codes)
  *   Wq, w_scale                from rudder_quantize_weights (same K, N, codes)
  *   codes      RUDDER_CODES_INT: int4 weights widened to int8 in registers
- *              feed int8 MFMA with int32 accumulation; RUDDER_CODES_E2M3
- *              (abits = 4): E2M3-held 4-bit codes feed the f8f6f4 MFMA with
- *              fp32 accumulation, exact for these integer operands
+ *              feed int8 MFMA with int32 accumulation; RUDDER_CODES_E2M3:
+ *              E2M3-held codes feed the f8f6f4 MFMA with fp32 accumulation,
+ *              exact for these integer operands (abits = 8: two MFMAs per
+ *              product, one per digit plane)
  *   comp_a, comp_b  fp32 [S][N]: the compensation of this (layer, step);
  *              y = a * t + b as one fp32 fma, the layer bias folded into b
  *   M >= 0 (M = 0 is a no-op), N > 0 multiple of 32, K > 0 multiple of 128,
@@ -198,9 +220,10 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
  * repeated reads; for some row counts its last blocks take the last rows in
  * narrower pieces); for M <= 256 one weight-streaming kernel.  On `stream`.
  * Errors: INVALID_ARG for a null required pointer, M < 0, N or K <= 0,
- * N % 32 != 0, S outside 1..8, abits not 4 or 8, an unknown container or
- * E2M3 with abits = 8, Xq/Wq/w_scale/comp_a/comp_b/Y/acc_out not 16-byte
- * aligned; UNSUPPORTED for K % 128 != 0 or K > RUDDER_MAX_K.
+ * N % 32 != 0, S outside 1..8, abits not 4 or 8, an unknown container,
+ * Xq/Wq/w_scale/comp_a/comp_b/Y/acc_out not 16-byte aligned; UNSUPPORTED for
+ * K % 128 != 0, K > RUDDER_MAX_K, or K > RUDDER_MAX_K_E2M3_A8 with E2M3
+ * codes and abits = 8.
  */
 rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint8_t* stream_id,
                               const uint8_t* Wq, const float* w_scale,
@@ -233,8 +256,10 @@ rudder_status_t rudder_linear(const void* Xq, const float* row_scale, const uint
  *   next_row_scale  out: fp32 [M] = D'[stream_id[m]]
  * Errors: those of rudder_linear, plus INVALID_ARG for a null
  * next_inv_smooth/next_act_scale/next_Xq/next_row_scale, next_abits not 4 or
- * 8, an unknown next container or E2M3 with next_abits = 8 or N % 64 != 0,
- * next_inv_smooth/next_Xq not 16-byte aligned.
+ * 8, an unknown next container or E2M3 with N % 64 != 0,
+ * next_inv_smooth/next_Xq not 16-byte aligned; UNSUPPORTED for E2M3 with
+ * abits = 8 or next_abits = 8 (8-bit E2M3 codes are not built for this
+ * path).
  */
 rudder_status_t rudder_linear_gelu_quant(const void* Xq, const float* row_scale,
                                          const uint8_t* stream_id, const uint8_t* Wq,

@@ -42,12 +42,15 @@ double rudder_mfma_ceiling_ops(int iters, int codes);
  * MFMAs (8 per set) on them.  The same matrix-core instruction as
  * rudder_linear with the same (abits, codes): int8 MFMA for
  * RUDDER_CODES_INT (int4 codes widened), FP6 f8f6f4 MFMA for
- * RUDDER_CODES_E2M3.  `sink` (rudder_mfma_ceiling_sink_bytes(), 16-byte
+ * RUDDER_CODES_E2M3 (abits = 8: one pair of MFMAs per product, one per
+ * digit plane, from one set of 2 weight and 4 two-plane activation fragments
+ * run twice per iteration; the op count per iteration is the same).
+ * `sink` (rudder_mfma_ceiling_sink_bytes(), 16-byte
  * aligned) receives per-thread checksums so that no work is elided; its
  * values carry no meaning.  Time the launch on `stream` and divide
  * rudder_mfma_ceiling_ops(iters, codes) by its duration.
  * Returns RUDDER_ERR_INVALID_ARG for null or misaligned pointers, abits not
- * 4 / 8, an unknown container or E2M3 with abits 8, M <= 0, N not a positive
+ * 4 / 8, an unknown container, M <= 0, N not a positive
  * multiple of 32, K not a positive multiple of 32 (64 for E2M3), or iters
  * outside 1..2^24; the code buffers must hold at least
  * rudder_packed_act_bytes(M, K, abits, codes) and

@@ -8,7 +8,7 @@ from typing import Dict, Optional
 import numpy as np
 
 import oracle
-from tiled_layout import tile_codes, tile_codes_e2m3
+from tiled_layout import tile_codes, tile_codes_e2m3, tile_codes_e2m3_a8
 
 CODES_INT, CODES_E2M3 = 0, 1
 
@@ -16,7 +16,7 @@ CODES_INT, CODES_E2M3 = 0, 1
 def tile_for(codes_kind: int, codes: np.ndarray, bits: int) -> np.ndarray:
     """Oracle codes -> the byte layout the library writes for that container."""
     if codes_kind == CODES_E2M3:
-        return tile_codes_e2m3(codes)
+        return tile_codes_e2m3_a8(codes) if bits == 8 else tile_codes_e2m3(codes)
     return tile_codes(codes, bits)
 
 

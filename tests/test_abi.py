@@ -9,8 +9,9 @@ import re
 import numpy as np
 import pytest
 
-from tiled_layout import (E2M3_OF, e2m3_value, tile_codes, tile_codes_e2m3, untile_codes,
-                          untile_codes_e2m3)
+from tiled_layout import (E2M3_OF, digits_a8, e2m3_field, e2m3_value, tile_codes,
+                          tile_codes_e2m3, tile_codes_e2m3_a8, untile_codes, untile_codes_e2m3,
+                          untile_codes_e2m3_a8)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -53,7 +54,9 @@ def test_size_helpers(lib):
     assert r.packed_weight_bytes(96, 64, E) == 0
     assert r.packed_act_bytes(4192, 2048, 4, E) == 4192 * 2048 * 3 // 4
     assert r.packed_act_bytes(1, 128, 4, E) == 32 * 128 * 3 // 4
-    assert r.packed_act_bytes(64, 128, 8, E) == 0
+    assert r.packed_act_bytes(64, 128, 8, E) == 64 * 128 * 3 // 2   # two digit planes
+    assert r.packed_act_bytes(33, 128, 8, E) == 64 * 128 * 3 // 2
+    assert r.packed_act_bytes(64, 96, 8, E) == 0
     assert r.packed_weight_bytes(128, 64, 7) == 0
 
 
@@ -85,8 +88,10 @@ def _linear(lib, **kw):
     (dict(M=-1), 1), (dict(N=0), 1), (dict(K=0), 1), (dict(N=48), 1),
     (dict(S=0), 1), (dict(S=9), 1), (dict(abits=5), 1), (dict(abits=16), 1),
     (dict(K=96), 2), (dict(K=65536 + 128), 2),
-    (dict(codes=2), 1), (dict(codes=-1), 1), (dict(codes=1, abits=8), 1),
+    (dict(codes=2), 1), (dict(codes=-1), 1),
     (dict(codes=1, abits=4, K=96), 2),
+    # 8-bit E2M3 codes: fp32 sums exact only up to K = 16384
+    (dict(codes=1, abits=8, K=16384 + 128), 2),
 ])
 def test_linear_rejects(lib, kw, status):
     assert _linear(lib, **kw) == status
@@ -112,7 +117,7 @@ def _quant_act(lib, **kw):
     (dict(rs=None), 1), (dict(scale=None, ws=None), 1),
     (dict(M=-5), 1), (dict(K=0), 1), (dict(K=48), 1), (dict(S=0), 1), (dict(S=9), 1),
     (dict(abits=2), 1), (dict(K=65536 + 32), 2),
-    (dict(codes=3), 1), (dict(codes=1), 1), (dict(codes=1, abits=4, K=96), 1),
+    (dict(codes=3), 1), (dict(codes=1, K=96), 1), (dict(codes=1, abits=4, K=96), 1),
 ])
 def test_quant_act_rejects(lib, kw, status):
     assert _quant_act(lib, **kw) == status
@@ -208,9 +213,9 @@ def _gelu_quant(lib, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(ninv=None), 1), (dict(nd=None), 1), (dict(nxq=None), 1), (dict(nrs=None), 1),
     (dict(Wq=None), 1), (dict(nabits=5), 1), (dict(ncodes=2), 1),
-    (dict(ncodes=1, nabits=8), 1), (dict(ncodes=1, N=96), 1), (dict(nxq=P + 4), 1),
+    (dict(ncodes=1, nabits=8), 2), (dict(ncodes=1, N=96), 1), (dict(nxq=P + 4), 1),
     (dict(ninv=P + 8), 1), (dict(N=48), 1), (dict(S=9), 1), (dict(K=96), 2),
-    (dict(codes=1, abits=8), 1),
+    (dict(codes=1, abits=8), 2),
 ])
 def test_linear_gelu_quant_rejects(lib, kw, status):
     assert _gelu_quant(lib, **kw) == status
@@ -259,7 +264,56 @@ def test_mfma_ceiling_validation(lib):
         return lib.rudder_mfma_ceiling(a["Xq"], a["Wq"], a["M"], a["N"], a["K"], a["abits"],
                                        a["codes"], a["iters"], a["sink"], None)
     for kw in (dict(Xq=None), dict(Wq=None), dict(sink=None), dict(sink=P + 4), dict(M=0),
-               dict(N=48), dict(K=48), dict(abits=6), dict(codes=2), dict(codes=1, abits=8),
-               dict(codes=1, abits=4, K=96), dict(iters=0), dict(iters=(1 << 24) + 1)):
+               dict(N=48), dict(K=48), dict(abits=6), dict(codes=2),
+               dict(codes=1, abits=8, K=96), dict(codes=1, abits=4, K=96), dict(iters=0),
+               dict(iters=(1 << 24) + 1)):
         assert call(**kw) == 1, kw
         assert len(lib.rudder_last_error()) > 0
+
+
+def test_e2m3_digit_split_covers_int8():
+    """Every 8-bit code splits into digits whose halves are exact E2M3 values
+    and recombine to the code; the encoder agrees with the integer table and
+    with the format's decode rule on all 64 fields."""
+    q = np.arange(-127, 128)
+    hi, lo = digits_a8(q)
+    assert np.array_equal(16 * hi + lo, q)
+    assert lo.min() == -8 and lo.max() == 7 and hi.min() == -8 and hi.max() == 8
+    for v in (hi / 2.0, lo / 2.0):
+        f = e2m3_field(v)
+        assert np.array_equal(e2m3_value(f), v)
+    # the encoder reproduces the integer table, and every field round-trips
+    for v, enc in E2M3_OF.items():
+        assert e2m3_field(np.array([float(v)]))[0] == enc
+        if v:
+            assert e2m3_field(np.array([-float(v)]))[0] == enc | 0x20
+    vals = e2m3_value(np.arange(64))
+    nz = vals != 0
+    assert np.array_equal(e2m3_field(vals[nz]), np.arange(64)[nz])
+    # the recombination 32 * (h/2) + 2 * (l/2) the matrix cores form under
+    # block scales 2^5 and 2^1
+    assert np.array_equal(32 * (hi / 2.0) + 2 * (lo / 2.0), q)
+
+
+def test_e2m3_a8_layout_roundtrip_and_slots():
+    """Two-plane layout of 8-bit codes: round trip, padding, and one slot of
+    each plane decoded by hand from the header's definition."""
+    rng = np.random.default_rng(3)
+    R, K = 45, 192
+    c = rng.integers(-127, 128, (R, K)).astype(np.int8)
+    c[0, :8] = [-127, 127, -8, 8, -9, 7, 0, -1]
+    buf = tile_codes_e2m3_a8(c)
+    assert buf.size == 64 * K * 3 // 2
+    back = untile_codes_e2m3_a8(buf, R, K)
+    assert np.array_equal(back[:R], c) and np.all(back[R:] == 0)
+    # row 37, k = 64*2 + 32 + t  ->  block 1*3+2 of 3072 bytes, slot 5+32
+    blk = (1 * (K // 64) + 2) * 3072
+    slot = 5 + 32
+    hi, lo = digits_a8(c[37, 160:192])
+    for plane, want in ((0, hi / 2.0), (1, lo / 2.0)):
+        base = blk + 1536 * plane
+        p0 = buf[base + 16 * slot: base + 16 * slot + 16]
+        p1 = buf[base + 1024 + 8 * slot: base + 1024 + 8 * slot + 8]
+        bits = int.from_bytes(bytes(p0) + bytes(p1), "little")
+        for t in range(32):
+            assert e2m3_value(np.array([(bits >> (6 * t)) & 0x3F]))[0] == want[t]

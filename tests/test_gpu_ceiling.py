@@ -6,7 +6,7 @@ import pytest
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("abits,codes", [(8, 0), (4, 0), (4, 1)])
+@pytest.mark.parametrize("abits,codes", [(8, 0), (4, 0), (4, 1), (8, 1)])
 def test_mfma_ceiling_runs_and_is_deterministic(abits, codes):
     import torch
     from w4a4_quantized_gemm_rudder_amd import rudder

@@ -80,6 +80,21 @@ RAGGED_E2M3 = [
 ]
 
 
+# W4A8 with the 8-bit codes held as two E2M3 digit planes (K a multiple of
+# 128): one, three and five k-stages, tails, 1..8 streams
+RAGGED_E2M3_A8 = [
+    (1, 128, 32, 1, 8, False, 70),
+    (33, 256, 64, 3, 8, True, 71),
+    (255, 256, 256, 8, 8, False, 72),
+    (257, 512, 320, 3, 8, True, 73),
+    (300, 128, 256, 3, 8, False, 74),
+    (301, 384, 512, 4, 8, True, 75),
+    (520, 640, 288, 2, 8, False, 76),
+    (600, 256, 544, 2, 8, True, 77),
+    (97, 1024, 1024, 7, 8, False, 78),
+]
+
+
 def _random_layer_case(M, K, N, S, abits, dynamic, seed, codes):
     rng = np.random.default_rng(1000 + seed)
     x = rng.standard_normal((M, K))
@@ -105,7 +120,8 @@ def _random_layer_case(M, K, N, S, abits, dynamic, seed, codes):
 
 @pytest.mark.parametrize("M,K,N,S,abits,dynamic,seed,codes",
                          [r + (CODES_INT,) for r in RAGGED] +
-                         [r + (CODES_E2M3,) for r in RAGGED_E2M3])
+                         [r + (CODES_E2M3,) for r in RAGGED_E2M3] +
+                         [r + (CODES_E2M3,) for r in RAGGED_E2M3_A8])
 def test_ragged_shapes(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case ragged M={M} K={K} N={N} S={S} abits={abits} dynamic={dynamic} seed={seed} "
         f"codes={codes}")
@@ -132,6 +148,11 @@ SMALL_M = [
     (192, 256, 16384, 3, 4, False, 31, CODES_E2M3),
     (250, 256, 16384, 3, 8, True, 32, CODES_INT),
     (60, 256, 16384, 2, 4, False, 33, CODES_INT),
+    # 8-bit codes as E2M3 digit planes (64-row groups only)
+    (96, 2048, 6144, 3, 8, True, 34, CODES_E2M3),
+    (192, 2048, 2048, 3, 8, False, 35, CODES_E2M3),
+    (250, 256, 16384, 3, 8, True, 36, CODES_E2M3),
+    (2, 256, 64, 2, 8, False, 37, CODES_E2M3),
 ]
 
 
@@ -153,6 +174,8 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     (8384, 256, 2048, 3, 4, False, 43, CODES_E2M3),     # 192-row remainder
     (8384, 512, 4096, 3, 8, True, 48, CODES_INT),       # two full rounds, 4096 wide
     (8292, 384, 4096, 4, 4, False, 49, CODES_E2M3),
+    (8292, 128, 2048, 3, 8, False, 56, CODES_E2M3),     # 8-bit codes as digit planes
+    (8384, 256, 2048, 3, 8, True, 57, CODES_E2M3),
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")
@@ -181,7 +204,8 @@ def test_round_remainder_narrow_tiles(M, K, N, S, abits, dynamic, seed, codes):
 # wave in one call: whole 128-row waves of one stream, run boundaries inside
 # a wave and on a wave boundary, a single row of another stream inside a run,
 # and a ragged last tile.
-@pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3)])
+@pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3),
+                                         (8, CODES_E2M3)])
 def test_stream_runs_uniform_and_mixed_waves(abits, codes):
     M, K, N, S = 700, 256, 512, 4
     rng = np.random.default_rng(60 + abits + codes)
@@ -208,14 +232,17 @@ def test_stream_runs_uniform_and_mixed_waves(abits, codes):
     log(f"  {run.run_step(delta, a, b, label='runs')}")
 
 
-@pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3)])
-def test_saturated_codes_at_max_k(abits, codes):
-    """K = 65536 (the largest supported) with every weight and activation code
-    at +-qmax: the accumulators reach 65536 * 7 * qmax in magnitude and must
-    still be exact."""
-    log(f"case saturated K=65536 abits={abits} codes={codes}")
+@pytest.mark.parametrize("abits,codes,K,M", [(8, CODES_INT, 65536, 40), (4, CODES_INT, 65536, 40),
+                                             (4, CODES_E2M3, 65536, 40),
+                                             (8, CODES_E2M3, 16384, 40),
+                                             (8, CODES_E2M3, 16384, 300)])
+def test_saturated_codes_at_max_k(abits, codes, K, M):
+    """The largest supported K (65536; 16384 for 8-bit E2M3 codes) with every
+    weight and activation code at +-qmax: the accumulators reach K * 7 * qmax
+    in magnitude and must still be exact (few-row and tiled kernels)."""
+    log(f"case saturated K={K} M={M} abits={abits} codes={codes}")
     rng = np.random.default_rng(99)
-    M, K, N, S = 40, 65536, 64, 2
+    N, S = 64, 2
     sx = np.where(rng.random((M, K)) < 0.5, -1.0, 1.0)
     sw = np.where(rng.random((K, N)) < 0.5, -1.0, 1.0)
     sw[:, :4] = 1.0                               # some columns of all-equal signs
@@ -301,6 +328,8 @@ FULL = [
     ("dit_block_h2048_m8384_16step", "down", [0, 11, 15], CODES_INT),
     ("dit_block_h2048_m8384_16step", "up", [2], CODES_E2M3),
     ("dit_block_h2048_m8384_16step", "down", [9, 15], CODES_E2M3),
+    ("dit_block_h2048_m8384_16step", "qkv", [0], CODES_E2M3),
+    ("dit_block_h2048_m8384_16step", "o", [6], CODES_E2M3),
     ("backbone_h4096_m16576_w4a4", "qkv", [0], CODES_INT),
     ("backbone_h4096_m16576_w4a4", "o", [19], CODES_INT),
     ("backbone_h4096_m16576_w4a4", "up", [4], CODES_INT),

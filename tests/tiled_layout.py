@@ -6,7 +6,8 @@ Block (rb, kb) covers rows 32rb..32rb+31 and k 32kb..32kb+31 and sits at
 block index rb*(K/32)+kb; slot l = (r%32) + 32*((k%32)//16) holds the 16 codes
 k = 32kb + 16*(l//32) + j.  8-bit: 16 bytes, byte j = code j.  4-bit: 8 bytes =
 two split-nibble words (codes 8w..8w+7; byte i holds code 8w+i low, 8w+4+i high).
-Rows R..ceil(R/32)*32-1 are zero padding.
+Rows R..ceil(R/32)*32-1 are zero padding.  The E2M3 container (4-bit codes,
+and 8-bit codes as two digit planes) follows below.
 """
 import numpy as np
 
@@ -82,11 +83,46 @@ def e2m3_value(code6: np.ndarray) -> np.ndarray:
     return sign * mag
 
 
+def e2m3_field(v: np.ndarray) -> np.ndarray:
+    """Encode values exactly representable in E2M3 as 6-bit fields, from the
+    format's definition: |v| = m/8 (exponent field 0) or (1 + m/8) 2^(e-1)
+    (exponent field e = 1..3), sign in bit 5, zero as 0x00."""
+    v = np.asarray(v, np.float64)
+    mag = np.abs(v)
+    e = np.where(mag < 1.0, 0, np.floor(np.log2(np.maximum(mag, 1.0))) + 1).astype(np.int64)
+    m = np.where(e == 0, mag * 8.0, (mag / 2.0 ** (np.maximum(e, 1) - 1) - 1.0) * 8.0)
+    assert np.all(e <= 3) and np.all(m == np.round(m)) and np.all(m < 8), "not exact in E2M3"
+    sign = np.where((v < 0) & (mag > 0), 0x20, 0)
+    return (sign | (e << 3) | m.astype(np.int64)).astype(np.uint8)
+
+
+def digits_a8(codes: np.ndarray):
+    """8-bit codes q -> the digits (h, l) of q = 16 h + l, l = ((q + 8) mod 16) - 8."""
+    q = np.asarray(codes, np.int64)
+    lo = np.mod(q + 8, 16) - 8
+    hi = (q - lo) // 16
+    return hi, lo
+
+
 def tile_codes_e2m3(codes: np.ndarray) -> np.ndarray:
     codes = _pad_rows(np.asarray(codes, np.int8))
-    Rp, K = codes.shape
-    assert K % 64 == 0
     enc = np.vectorize(lambda v: E2M3_OF[abs(int(v))] | (0x20 if v < 0 else 0))(codes)
+    return _tile_fields_e2m3(enc).reshape(-1)
+
+
+def tile_codes_e2m3_a8(codes: np.ndarray) -> np.ndarray:
+    """8-bit codes -> 3072-byte blocks: the h/2 block, then the l/2 block."""
+    codes = _pad_rows(np.asarray(codes, np.int8))
+    hi, lo = digits_a8(codes)
+    th = _tile_fields_e2m3(e2m3_field(hi / 2.0))
+    tl = _tile_fields_e2m3(e2m3_field(lo / 2.0))
+    return np.ascontiguousarray(np.concatenate([th, tl], axis=-1)).reshape(-1)
+
+
+def _tile_fields_e2m3(enc: np.ndarray) -> np.ndarray:
+    """6-bit fields [Rp, K] -> blocks [Rp/32, K/64, 1536]."""
+    Rp, K = enc.shape
+    assert K % 64 == 0 and Rp % 32 == 0
     enc = enc.astype(np.uint64)
     # [rb, r32, kb, half, t] -> [rb, kb, half, r32, t]
     t = enc.reshape(Rp // 32, 32, K // 64, 2, 32).transpose(0, 2, 3, 1, 4)
@@ -102,13 +138,11 @@ def tile_codes_e2m3(codes: np.ndarray) -> np.ndarray:
     b = b.reshape(Rp // 32, K // 64, 64, 24)                      # slot = r32 + 32*half
     out = np.concatenate([b[..., :16].reshape(Rp // 32, K // 64, 1024),
                           b[..., 16:].reshape(Rp // 32, K // 64, 512)], axis=-1)
-    return np.ascontiguousarray(out).reshape(-1)
+    return np.ascontiguousarray(out)
 
 
-def untile_codes_e2m3(buf: np.ndarray, R: int, K: int) -> np.ndarray:
-    Rp = (R + 31) // 32 * 32
-    blk = np.asarray(buf, np.uint8).reshape(-1)[: Rp * K * 3 // 4].reshape(Rp // 32, K // 64,
-                                                                             1536)
+def untile_values_e2m3(blk: np.ndarray, Rp: int, K: int) -> np.ndarray:
+    """Blocks [Rp/32, K/64, 1536] -> decoded E2M3 values [Rp, K]."""
     p0 = blk[..., :1024].reshape(Rp // 32, K // 64, 64, 16)
     p1 = blk[..., 1024:].reshape(Rp // 32, K // 64, 64, 8)
     b = np.concatenate([p0, p1], axis=-1)                          # [rb, kb, slot, 24]
@@ -121,7 +155,26 @@ def untile_codes_e2m3(buf: np.ndarray, R: int, K: int) -> np.ndarray:
         if off > 58:
             v |= words[..., w + 1] << np.uint64(64 - off)
         vals[..., ti] = (v & np.uint64(0x3F)).astype(np.int64)
-    dec = e2m3_value(vals)
+    dec = e2m3_value(vals).reshape(Rp // 32, K // 64, 2, 32, 32)      # [rb, kb, half, r32, t]
+    return np.ascontiguousarray(dec.transpose(0, 3, 1, 2, 4)).reshape(Rp, K)
+
+
+def untile_codes_e2m3(buf: np.ndarray, R: int, K: int) -> np.ndarray:
+    Rp = (R + 31) // 32 * 32
+    blk = np.asarray(buf, np.uint8).reshape(-1)[: Rp * K * 3 // 4].reshape(Rp // 32, K // 64,
+                                                                             1536)
+    dec = untile_values_e2m3(blk, Rp, K)
     assert np.all(dec == np.round(dec)) and np.all(np.abs(dec) <= 7.5)
-    codes = dec.astype(np.int8).reshape(Rp // 32, K // 64, 2, 32, 32)   # [rb, kb, half, r32, t]
-    return np.ascontiguousarray(codes.transpose(0, 3, 1, 2, 4)).reshape(Rp, K)
+    return dec.astype(np.int8)
+
+
+def untile_codes_e2m3_a8(buf: np.ndarray, R: int, K: int) -> np.ndarray:
+    """3072-byte digit blocks -> 8-bit codes 32 * (h/2) + 2 * (l/2)."""
+    Rp = (R + 31) // 32 * 32
+    blk = np.asarray(buf, np.uint8).reshape(-1)[: Rp * K * 3 // 2].reshape(Rp // 32, K // 64,
+                                                                             3072)
+    h2 = untile_values_e2m3(np.ascontiguousarray(blk[..., :1536]), Rp, K)
+    l2 = untile_values_e2m3(np.ascontiguousarray(blk[..., 1536:]), Rp, K)
+    q = 32.0 * h2 + 2.0 * l2
+    assert np.all(q == np.round(q)) and np.all(np.abs(q) <= 127)
+    return q.astype(np.int8)

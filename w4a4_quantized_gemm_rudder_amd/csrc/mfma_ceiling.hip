@@ -57,8 +57,13 @@ __device__ __forceinline__ v4i widen(uint2 w) {
                (int)((w.y << 4) & 0xF0F0F0F0u), (int)(w.y & 0xF0F0F0F0u)};
 }
 
+// E8M0 scale bytes 2^0, 2^5 and 2^1 in one word (op_sel picks the byte), as
+// the GEMM passes them for 8-bit codes in the E2M3 container.
+constexpr int kDigitScaleWord = 127 | (127 + 5) << 8 | (127 + 1) << 16;
+
 // ABITS 8: int8 activations x int4 weights (int8 MFMA); ABITS 4 with
-// E2M3 = false: int4 x int4 widened to int8; E2M3: FP6 f8f6f4 MFMA.
+// E2M3 = false: int4 x int4 widened to int8; E2M3: FP6 f8f6f4 MFMA (ABITS
+// 8: two MFMAs per product, one per digit plane of the activation codes).
 template <int ABITS, bool E2M3>
 __global__ __launch_bounds__(kThreads, 2) void mfma_ceiling_kernel(
     const uint8_t* __restrict__ Xq, uint32_t act_blocks, const uint8_t* __restrict__ Wq,
@@ -66,7 +71,49 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_ceiling_kernel(
     const int lane = threadIdx.x & 63;
     const uint32_t w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
     int32_t out = 0;
-    if constexpr (E2M3) {
+    if constexpr (E2M3 && ABITS == 8) {
+        // one set of fragments (both planes of each activation block), run
+        // twice per iteration: 16 digit-plane pairs, the same products per
+        // iteration as the other forms
+        v6i wf[kFW], ah[kFA], al[kFA];
+#pragma unroll
+        for (int f = 0; f < kFW + kFA; ++f) {
+            const bool is_w = f < kFW;
+            const uint8_t* blk = is_w ? Wq + (size_t)pick_block(w, f, w_blocks) * 1536
+                                      : Xq + (size_t)pick_block(w, f, act_blocks) * 3072;
+#pragma unroll
+            for (int p = 0; p < (is_w ? 1 : 2); ++p) {
+                const uint8_t* b = blk + p * 1536;
+                const v4i p0 = *reinterpret_cast<const v4i*>(b + lane * 16);
+                const v2i p1 = *reinterpret_cast<const v2i*>(b + 1024 + lane * 8);
+                const v6i v = __builtin_shufflevector(
+                    p0, __builtin_shufflevector(p1, p1, 0, 1, -1, -1), 0, 1, 2, 3, 4, 5);
+                if (is_w) wf[f] = v;
+                else if (p == 0) ah[f - kFW] = v;
+                else al[f - kFW] = v;
+            }
+        }
+        v16f acc[kFW][kFA] = {};
+        for (int it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int s = 0; s < kSets; ++s)
+#pragma unroll
+                for (int f = 0; f < kFW; ++f)
+#pragma unroll
+                    for (int g = 0; g < kFA; ++g) {
+                        acc[f][g] = mfma_scale_f32_32x32x64_fp6(wf[f], ah[g], acc[f][g], 2, 2, 0,
+                                                                kDigitScaleWord, 1,
+                                                                kDigitScaleWord);
+                        acc[f][g] = mfma_scale_f32_32x32x64_fp6(wf[f], al[g], acc[f][g], 2, 2, 0,
+                                                                kDigitScaleWord, 2,
+                                                                kDigitScaleWord);
+                    }
+        }
+#pragma unroll
+        for (int f = 0; f < kFW; ++f)
+#pragma unroll
+            for (int g = 0; g < kFA; ++g) out += __float_as_int(acc[f][g][lane & 15]);
+    } else if constexpr (E2M3) {
         v6i wf[kSets][kFW], af[kSets][kFA];
 #pragma unroll
         for (int s = 0; s < kSets; ++s) {
@@ -160,7 +207,10 @@ hipError_t launch_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M, int 
     const uint32_t act_blocks = (uint32_t)((M + 31) / 32) * kb;
     const uint32_t w_blocks = (uint32_t)(N / 32) * kb;
     const dim3 grid(RUDDER_CEILING_BLOCKS), block(kThreads);
-    if (codes == RUDDER_CODES_E2M3)
+    if (codes == RUDDER_CODES_E2M3 && abits == 8)
+        hipLaunchKernelGGL((mfma_ceiling_kernel<8, true>), grid, block, 0, stream, Xq, act_blocks,
+                           Wq, w_blocks, iters, sink);
+    else if (codes == RUDDER_CODES_E2M3)
         hipLaunchKernelGGL((mfma_ceiling_kernel<4, true>), grid, block, 0, stream, Xq, act_blocks,
                            Wq, w_blocks, iters, sink);
     else if (abits == 8)

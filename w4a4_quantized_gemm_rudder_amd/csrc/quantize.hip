@@ -190,11 +190,15 @@ __global__ __launch_bounds__(kThreads) void quant_act_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Activation quantizer, E2M3 container (4-bit codes).  One wave per 32 x 64
-// (row, k) block: lane l handles row 32rb + l % 32 and the 32 k starting at
-// 64kb + 32 (l / 32); plane 0 and plane 1 of the block are each written
-// contiguously by the wave.
+// Activation quantizer, E2M3 container.  One wave per 32 x 64 (row, k)
+// block: lane l handles row 32rb + l % 32 and the 32 k starting at
+// 64kb + 32 (l / 32); plane 0 and plane 1 of each 1536-byte block are each
+// written contiguously by the wave.  4-bit codes: one block of the codes.
+// 8-bit codes q: two blocks, the digits of q = 16 h + l with
+// l = ((q + 8) mod 16) - 8 in [-8, 7] and h = (q - l) / 16 in [-8, 8], held
+// as the exact E2M3 values h / 2 and l / 2.
 // ---------------------------------------------------------------------------
+template <int ABITS>
 __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
     const uint16_t* __restrict__ X, const uint8_t* __restrict__ sid,
     const float* __restrict__ inv_smooth, const float* __restrict__ delta, int M, int K, int S,
@@ -253,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
             for (int i = 0; i < 16; ++i) {
                 const uint32_t hbits = (i & 1) ? (xw[i >> 1] >> 16) : (xw[i >> 1] & 0xFFFFu);
                 const float u = bf16_bits_to_float(hbits) * is[i];
-                c[16 * h + i] = quantize_clamped_f(u * ia, 7.0f);
+                c[16 * h + i] = quantize_clamped_f(u * ia, ABITS == 8 ? 127.0f : 7.0f);
             }
         }
         if (kb == 0 && lane < 32) row_scale[r] = s_delta[s];
@@ -261,15 +265,35 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
 #pragma unroll
         for (int i = 0; i < 32; ++i) c[i] = 0.0f;
     }
-    uint32_t d[6];
-    pack_e2m3x32(c, d);
     // Streaming stores: the E2M3 GEMM that reads these codes runs 2-3%
     // faster than after write-back stores (the int codecs' GEMMs run
     // slower, and those codecs keep plain stores).
-    uint8_t* blk = Xq + e2m3_block_offset(r, k0, K);
     const int slot = e2m3_slot(r, k0);
-    nt_store16(blk + slot * 16, make_uint4(d[0], d[1], d[2], d[3]));
-    nt_store8(blk + 1024 + slot * 8, make_uint2(d[4], d[5]));
+    if constexpr (ABITS == 8) {
+        float ch[32], cl[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int q = (int)c[i];
+            const int lo = ((q + 8) & 15) - 8;
+            const int hi = (q - lo) / 16;
+            ch[i] = (float)hi * 0.5f;
+            cl[i] = (float)lo * 0.5f;
+        }
+        uint32_t dh[6], dl[6];
+        pack_e2m3x32(ch, dh);
+        pack_e2m3x32(cl, dl);
+        uint8_t* blk = Xq + 2 * e2m3_block_offset(r, k0, K);
+        nt_store16(blk + slot * 16, make_uint4(dh[0], dh[1], dh[2], dh[3]));
+        nt_store8(blk + 1024 + slot * 8, make_uint2(dh[4], dh[5]));
+        nt_store16(blk + 1536 + slot * 16, make_uint4(dl[0], dl[1], dl[2], dl[3]));
+        nt_store8(blk + 1536 + 1024 + slot * 8, make_uint2(dl[4], dl[5]));
+    } else {
+        uint32_t d[6];
+        pack_e2m3x32(c, d);
+        uint8_t* blk = Xq + e2m3_block_offset(r, k0, K);
+        nt_store16(blk + slot * 16, make_uint4(d[0], d[1], d[2], d[3]));
+        nt_store8(blk + 1024 + slot * 8, make_uint2(d[4], d[5]));
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -375,9 +399,13 @@ hipError_t launch_quant_act_static(const uint16_t* X, const uint8_t* sid, const 
                                    void* Xq, float* row_scale, hipStream_t stream) {
     if (codes == RUDDER_CODES_E2M3) {
         const long waves = (long)((M + 31) / 32) * (K / 64);
-        hipLaunchKernelGGL(quant_act_e2m3_kernel, dim3((unsigned)((waves + 3) / 4)),
-                           dim3(kThreads), 0, stream, X, sid, inv_smooth, delta, M, K, S,
-                           static_cast<uint8_t*>(Xq), row_scale);
+        const dim3 grid((unsigned)((waves + 3) / 4));
+        if (abits == 8)
+            hipLaunchKernelGGL(quant_act_e2m3_kernel<8>, grid, dim3(kThreads), 0, stream, X, sid,
+                               inv_smooth, delta, M, K, S, static_cast<uint8_t*>(Xq), row_scale);
+        else
+            hipLaunchKernelGGL(quant_act_e2m3_kernel<4>, grid, dim3(kThreads), 0, stream, X, sid,
+                               inv_smooth, delta, M, K, S, static_cast<uint8_t*>(Xq), row_scale);
         return hipGetLastError();
     }
     const long waves = (long)((M + 31) / 32) * (K / 32);

@@ -51,8 +51,8 @@ size_t rudder_packed_act_bytes(int M, int K, int abits, int codes) {
     if (M < 0 || K <= 0 || K % 32 || (abits != 4 && abits != 8)) return 0;
     const size_t rows = (size_t)((M + 31) / 32) * 32;
     if (codes == RUDDER_CODES_INT) return rows * (size_t)K * (size_t)abits / 8;
-    if (codes == RUDDER_CODES_E2M3 && abits == 4 && K % 64 == 0)
-        return rows * (size_t)K * 3 / 4;
+    if (codes == RUDDER_CODES_E2M3 && K % 64 == 0)
+        return rows * (size_t)K * 3 / 4 * (abits == 8 ? 2 : 1);
     return 0;
 }
 
@@ -106,10 +106,9 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
         return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
     if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
-    if (codes == RUDDER_CODES_E2M3 && (abits != 4 || K % 64))
-        return fail(RUDDER_ERR_INVALID_ARG,
-                    "%s: E2M3 codes need abits=4 and K a multiple of 64 (abits=%d, K=%d)", f,
-                    abits, K);
+    if (codes == RUDDER_CODES_E2M3 && K % 64)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 64 for E2M3 codes",
+                    f, K);
     if (misaligned(X) || misaligned(inv_smooth) || misaligned(Xq) || misaligned(workspace))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: X, inv_smooth, Xq and workspace must be "
                     "16-byte aligned", f);
@@ -147,8 +146,6 @@ rudder_status_t check_linear(const char* f, const void* Xq, const float* row_sca
         return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
     if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
-    if (codes == RUDDER_CODES_E2M3 && abits != 4)
-        return fail(RUDDER_ERR_INVALID_ARG, "%s: E2M3 codes need abits=4 (abits=%d)", f, abits);
     if (misaligned(Xq) || misaligned(Wq) || misaligned(w_scale) || misaligned(comp_a) ||
         misaligned(comp_b))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: Xq, Wq, w_scale, comp_a and comp_b must be "
@@ -157,6 +154,9 @@ rudder_status_t check_linear(const char* f, const void* Xq, const float* row_sca
         return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d is not a multiple of 128", f, K);
     if (K > RUDDER_MAX_K)
         return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
+    if (codes == RUDDER_CODES_E2M3 && abits == 8 && K > RUDDER_MAX_K_E2M3_A8)
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d for 8-bit E2M3 codes", f, K,
+                    RUDDER_MAX_K_E2M3_A8);
     return RUDDER_OK;
 }
 
@@ -195,16 +195,19 @@ rudder_status_t rudder_linear_gelu_quant(const void* Xq, const float* row_scale,
         return fail(RUDDER_ERR_INVALID_ARG, "%s: next_abits=%d must be 4 or 8", f, next_abits);
     if (next_codes != RUDDER_CODES_INT && next_codes != RUDDER_CODES_E2M3)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, next_codes);
-    if (next_codes == RUDDER_CODES_E2M3 && (next_abits != 4 || N % 64))
+    if (next_codes == RUDDER_CODES_E2M3 && N % 64)
         return fail(RUDDER_ERR_INVALID_ARG,
-                    "%s: E2M3 next codes need next_abits=4 and N a multiple of 64 (%d, N=%d)", f,
-                    next_abits, N);
+                    "%s: E2M3 next codes need N a multiple of 64 (N=%d)", f, N);
     if (misaligned(next_inv_smooth) || misaligned(next_Xq))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: next_inv_smooth and next_Xq must be 16-byte "
                     "aligned", f);
     const rudder_status_t st = check_linear(f, Xq, row_scale, stream_id, Wq, w_scale, comp_a,
                                             comp_b, M, N, K, S, abits, codes);
     if (st != RUDDER_OK) return st;
+    if ((codes == RUDDER_CODES_E2M3 && abits == 8) ||
+        (next_codes == RUDDER_CODES_E2M3 && next_abits == 8))
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: 8-bit E2M3 codes are not built for this path",
+                    f);
     if (M == 0) return ok();
     const rudder::NextLayerQuant next{next_inv_smooth, next_act_scale,
                                       static_cast<uint8_t*>(next_Xq), next_row_scale, next_abits,
@@ -275,8 +278,6 @@ rudder_status_t rudder_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M,
         return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
     if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
         return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
-    if (codes == RUDDER_CODES_E2M3 && abits != 4)
-        return fail(RUDDER_ERR_INVALID_ARG, "%s: E2M3 codes need abits=4", f);
     const int kmul = codes == RUDDER_CODES_E2M3 ? 64 : 32;
     if (M <= 0 || N <= 0 || K <= 0 || N % 32 || K % kmul)
         return fail(RUDDER_ERR_INVALID_ARG,

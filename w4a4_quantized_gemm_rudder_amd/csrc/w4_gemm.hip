@@ -40,7 +40,9 @@
 //     twice the int8 rate.  Products of codes are small integers and every
 //     fp32 partial sum is an integer below 2^24, so the fp32 accumulator holds
 //     the exact integer dot product.  Its operands are the 6-dword form the
-//     instruction takes for FP6, read straight into place.
+//     instruction takes for FP6, read straight into place.  8-bit codes in
+//     this container are two digit planes, one MFMA each under E8M0 scales
+//     2^5 and 2^1 (exact up to K = 16384).
 //   * Tile order: workgroups are dealt round-robin to the 8 XCDs; the grid is
 //     remapped so each XCD walks a contiguous, m-grouped range of tiles and
 //     the tiles in flight on one XCD share activation and weight panels in
@@ -56,7 +58,8 @@ typedef float mfma_v16f __attribute__((ext_vector_type(16)));
 // The f8f6f4 scaled MFMA with 6-dword operands, as the instruction takes them
 // for FP6 formats (the clang builtin fixes 8-dword operands, which would make
 // every fragment a padded 8-register tuple and cost register moves).  Called
-// with cbsz = blgp = 2 (FP6 E2M3 A and B) and unit E8M0 scales only.
+// with cbsz = blgp = 2 (FP6 E2M3 A and B) and power-of-two E8M0 scales
+// (unit, or the digit planes' 2^5 and 2^1).
 __device__ mfma_v16f mfma_scale_f32_32x32x64_fp6(mfma_v6i a, mfma_v6i b, mfma_v16f c,
                                                  int cbsz, int blgp, int opsel_a, int scale_a,
                                                  int opsel_b, int scale_b)
@@ -98,6 +101,11 @@ constexpr int kEpiE2M3 = 3;
 constexpr int kFmtA8 = 0;        // int8 activations, int4 weights (int8 MFMA)
 constexpr int kFmtA4 = 1;        // int4 activations and weights (int8 MFMA)
 constexpr int kFmtF6 = 2;        // 4-bit codes held as E2M3 (f8f6f4 MFMA)
+constexpr int kFmtD6 = 3;        // int8 activations as two E2M3 digit planes, E2M3 weights
+                                 // (f8f6f4 MFMA, two per product)
+
+// The formats whose operands are E2M3 fields (fp32 accumulators).
+constexpr bool fp6_fmt(int fmt) { return fmt == kFmtF6 || fmt == kFmtD6; }
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v6i __attribute__((ext_vector_type(6)));
@@ -107,7 +115,11 @@ typedef int v6i __attribute__((ext_vector_type(6)));
 // 128 x 256 block tile; each wave owns FW = 2 32-channel and FA = 4 32-token
 // fragments, so every k-substep it takes FW weight fragments (its own, from
 // registers) and FA activation fragments (shared, from LDS) and issues
-// FW * FA MFMAs.
+// FW * FA MFMAs per activation plane.  kPlanes activation planes share one
+// weight fragment: the digit format holds each int8 code q as q = 16 h + l
+// in two E2M3 planes (h / 2 and l / 2, both exact), and multiplies them with
+// E8M0 block scales 2^5 and 2^1 into the same fp32 accumulator, which then
+// holds sum q * w exactly.
 template <int FMT>
 struct Fmt;
 template <>
@@ -119,6 +131,7 @@ struct Fmt<kFmtA8> {
     typedef uint2 WFrag;
     typedef uint4 AFrag;
     typedef v16i Acc;
+    static constexpr int kPlanes = 1;
 };
 template <>
 struct Fmt<kFmtA4> {
@@ -129,6 +142,7 @@ struct Fmt<kFmtA4> {
     typedef uint2 WFrag;
     typedef uint2 AFrag;
     typedef v16i Acc;
+    static constexpr int kPlanes = 1;
 };
 template <>
 struct Fmt<kFmtF6> {
@@ -139,6 +153,30 @@ struct Fmt<kFmtF6> {
     typedef v6i WFrag;     // MFMA operand registers
     typedef v6i AFrag;
     typedef v16f Acc;
+    static constexpr int kPlanes = 1;
+    static constexpr int kPlaneBytes = 1536;
+    // E8M0 scales (127 = 2^0): the word passed as both scale operands, the
+    // byte the weights take and the byte activation plane p takes
+    static constexpr int kScaleWord = 127;
+    static constexpr int kWeightScaleSel = 0;
+    static constexpr int plane_scale_sel(int) { return 0; }
+};
+template <>
+struct Fmt<kFmtD6> {
+    static constexpr int kKSub = 64;
+    static constexpr int kABlock = 3072;   // high-digit plane, then low-digit plane
+    static constexpr int kWBlock = 1536;
+    static constexpr int kWavesN = 4;
+    typedef v6i WFrag;
+    typedef v6i AFrag;     // one plane
+    typedef v16f Acc;
+    static constexpr int kPlanes = 2;
+    static constexpr int kPlaneBytes = 1536;
+    // bytes 2^0, 2^5 (high digits), 2^1 (low digits) of one scale word, so
+    // that every MFMA takes its scales from one register
+    static constexpr int kScaleWord = 127 | (127 + 5) << 8 | (127 + 1) << 16;
+    static constexpr int kWeightScaleSel = 0;
+    static constexpr int plane_scale_sel(int p) { return p == 0 ? 1 : 2; }
 };
 
 template <int FMT, int TBN = BN>
@@ -284,7 +322,7 @@ __device__ __forceinline__ void read_frag<v6i>(const uint8_t* block, int lane, v
 // (W4A8) or 256x (W4A4) the true sum, see widen_nibbles).
 template <int FMT>
 __device__ __forceinline__ int acc_value(const typename Fmt<FMT>::Acc& a, int r) {
-    if constexpr (FMT == kFmtF6) return (int)a[r];
+    if constexpr (fp6_fmt(FMT)) return (int)a[r];
     else if constexpr (FMT == kFmtA8) return a[r] >> 4;
     else return a[r] >> 8;
 }
@@ -293,7 +331,7 @@ __device__ __forceinline__ int acc_value(const typename Fmt<FMT>::Acc& a, int r)
 // already hold it; the int containers shift and convert.
 template <int FMT>
 __device__ __forceinline__ float acc_float(const typename Fmt<FMT>::Acc& a, int r) {
-    if constexpr (FMT == kFmtF6) return a[r];
+    if constexpr (fp6_fmt(FMT)) return a[r];
     else return (float)acc_value<FMT>(a, r);
 }
 
@@ -330,7 +368,7 @@ __device__ __forceinline__ void gemm_tile(
     // compiler waits for them only in the epilogue).  The int formats fetch
     // them before the main loop; the E2M3 loop has no registers to hold them
     // across it, so it fetches them after the loop.
-    constexpr bool kLateRowData = FMT == kFmtF6;
+    constexpr bool kLateRowData = fp6_fmt(FMT);
     int row_stream[FA];
     float row_rs[FA];
     auto fetch_row_data = [&]() {
@@ -417,7 +455,8 @@ __device__ __forceinline__ void gemm_tile(
     static_assert(NS == 2, "direct-weight loop bookkeeping");
     constexpr int P = BK / F::kKSub;                  // substeps per stage
     static_assert(P % 2 == 0, "substep parity");
-    constexpr bool kF6 = FMT == kFmtF6;
+    constexpr bool kF6 = fp6_fmt(FMT);
+    constexpr int PL = F::kPlanes;                    // activation planes per substep
     constexpr int WL = kF6 ? 2 * FW : FW;             // weight loads per substep
     typedef typename F::WFrag WOp;
     typedef typename F::AFrag AOp;
@@ -446,21 +485,29 @@ __device__ __forceinline__ void gemm_tile(
             }
         }
     };
-    auto read_acts = [&](int kt, int kk, AOp (&dst)[FA]) {
-        const uint8_t* st = lds + (kt % NS) * C::kStageBytes + kk * C::kActBlock;
+    // js = kk * PL + plane: activation plane `plane` of substep kk
+    auto read_acts = [&](int kt, int js, AOp (&dst)[FA]) {
+        int plane_off = 0;
+        if constexpr (PL > 1) plane_off = (js % PL) * F::kPlaneBytes;
+        const uint8_t* st =
+            lds + (kt % NS) * C::kStageBytes + (js / PL) * C::kActBlock + plane_off;
 #pragma unroll
         for (int g = 0; g < FA; ++g) read_frag(st + (wm * FA + g) * C::kActPerMb, lane, dst[g]);
     };
-    auto mma = [&](const WOp (&w)[FW], const AOp (&a)[FA], int first, int last) {
+    auto mma = [&](const WOp (&w)[FW], const AOp (&a)[FA], int first, int last, auto plane_) {
+        constexpr int plane = decltype(plane_)::value;
 #pragma unroll
         for (int f = 0; f < FW; ++f) {
             if constexpr (kF6) {
-                // formats: 2 = FP6 E2M3 for both operands; scales 127 = 2^0 (E8M0)
+                // formats: 2 = FP6 E2M3 for both operands; E8M0 scales: 2^0
+                // for the weights, the plane's own for the activations
+                constexpr int sel = F::plane_scale_sel(plane);
 #pragma unroll
                 for (int g = 0; g < FA; ++g)
                     if (f * FA + g >= first && f * FA + g < last)
-                        acc[f][g] = mfma_scale_f32_32x32x64_fp6(w[f], a[g], acc[f][g], 2, 2, 0,
-                                                                127, 0, 127);
+                        acc[f][g] = mfma_scale_f32_32x32x64_fp6(
+                            w[f], a[g], acc[f][g], 2, 2, F::kWeightScaleSel, F::kScaleWord, sel,
+                            F::kScaleWord);
             } else {
                 if (f * FA + FA <= first || f * FA >= last) continue;
                 const v4i wf = widen_nibbles(w[f].x, w[f].y);
@@ -507,32 +554,39 @@ __device__ __forceinline__ void gemm_tile(
         const bool prefetch = kt + 2 <= klast;     // stage kt+2 exists
 #pragma unroll
         for (int kk = 0; kk < P; ++kk) {
-            // The substep's first MFMA goes ahead of the next reads.  It
-            // waits for the substep's activation fragments, all read a
-            // substep earlier; the explicit lgkmcnt(0) records that they
-            // have landed, so the remaining MFMAs, issued after the next
-            // reads, carry no wait on those reads.
-            mma(wreg[u][kk], fa[kk % 2], 0, 1);
-            asm volatile("" : "+v"(acc[0][0]));
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            if (kk + 1 < P) {
-                read_acts(kt, kk + 1, fa[(kk + 1) % 2]);
-            } else if (kt < klast) {
-                // Admit stage kt+1.  Its ring loads were issued at the
-                // previous boundary (in the prologue for kt = 0); after them
-                // came the weight refills of the substeps since then.
-                if (kt == 0) wait_and_barrier<(3 * P - 1) * WL>();
-                else wait_and_barrier<P * WL>();
-                if (kt + 2 < ksteps) issue_stage(kt + 2);
-                read_acts(kt + 1, 0, fa[0]);
-            }
-            mma(wreg[u][kk], fa[kk % 2], 1, FW * FA);
-            // keep this substep's MFMAs ahead of what follows (no sinking
-            // past the barrier or the slot refill)
+            // One activation plane of substep kk (js = kk * PL + plane).
+            auto plane_step = [&](auto pl_) {
+                constexpr int pl = decltype(pl_)::value;
+                const int js = kk * PL + pl;
+                // The first MFMA goes ahead of the next reads.  It waits for
+                // this plane's activation fragments, all read one plane
+                // earlier; the explicit lgkmcnt(0) records that they have
+                // landed, so the remaining MFMAs, issued after the next
+                // reads, carry no wait on those reads.
+                mma(wreg[u][kk], fa[js % 2], 0, 1, pl_);
+                asm volatile("" : "+v"(acc[0][0]));
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                if (js + 1 < P * PL) {
+                    read_acts(kt, js + 1, fa[(js + 1) % 2]);
+                } else if (kt < klast) {
+                    // Admit stage kt+1.  Its ring loads were issued at the
+                    // previous boundary (in the prologue for kt = 0); after
+                    // them came the weight refills of the substeps since then.
+                    if (kt == 0) wait_and_barrier<(3 * P - 1) * WL>();
+                    else wait_and_barrier<P * WL>();
+                    if (kt + 2 < ksteps) issue_stage(kt + 2);
+                    read_acts(kt + 1, 0, fa[0]);
+                }
+                mma(wreg[u][kk], fa[js % 2], 1, FW * FA, pl_);
+                // keep these MFMAs ahead of what follows (no sinking past
+                // the barrier or the slot refill)
 #pragma unroll
-            for (int f = 0; f < FW; ++f)
+                for (int f = 0; f < FW; ++f)
 #pragma unroll
-                for (int g = 0; g < FA; ++g) asm volatile("" : "+v"(acc[f][g]));
+                    for (int g = 0; g < FA; ++g) asm volatile("" : "+v"(acc[f][g]));
+            };
+            plane_step(std::integral_constant<int, 0>{});
+            if constexpr (PL > 1) plane_step(std::integral_constant<int, 1>{});
             load_w(min(kt + 2, klast), kk, wreg[u][kk], prefetch);
         }
     };
@@ -811,7 +865,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, int narrow_first, int narrow_m0,
     int touch_blocks, int tail_first, int tail_m0, NextLayerQuant nx) {
     if ((int)blockIdx.x < touch_blocks) {
-        const size_t bytes = FMT == kFmtF6 ? (size_t)N * K * 3 / 4 : (size_t)N * K / 2;
+        const size_t bytes = fp6_fmt(FMT) ? (size_t)N * K * 3 / 4 : (size_t)N * K / 2;
         const size_t lines = bytes / 128;
         const uint32_t* p = reinterpret_cast<const uint32_t*>(Wq);
         uint32_t v = 0;
@@ -836,7 +890,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             return;
         }
     }
-    if constexpr (EPI == kEpiBf16 && FMT != kFmtF6) {
+    if constexpr (EPI == kEpiBf16 && !fp6_fmt(FMT)) {
         if (bid >= narrow_first) {
             const int t = bid - narrow_first;
             const int rows = (M - narrow_m0 + BM - 1) / BM;       // narrow tile rows
@@ -873,12 +927,19 @@ constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 
 // Operand registers of one k-substep: NW weight fragments (NW consecutive
 // 32-channel blocks) and up to FA activation fragments, already in MFMA
-// operand form (E2M3 fragments are loaded straight into 6-dword operands).
+// operand form (E2M3 fragments are loaded straight into 6-dword operands;
+// the digit format's activation fragment is its two planes).
+struct F6Planes {
+    v6i p[2];
+};
 template <int FMT, int FA, int NW>
 struct SkinnyOps {
-    typedef typename std::conditional<FMT == kFmtF6, v6i, uint2>::type WOp;
-    typedef typename std::conditional<FMT == kFmtF6, v6i,
-            typename std::conditional<FMT == kFmtA8, uint4, uint2>::type>::type AOp;
+    typedef typename std::conditional<fp6_fmt(FMT), v6i, uint2>::type WOp;
+    typedef typename std::conditional<
+        FMT == kFmtD6, F6Planes,
+        typename std::conditional<FMT == kFmtF6, v6i,
+                                  typename std::conditional<FMT == kFmtA8, uint4,
+                                                            uint2>::type>::type>::type AOp;
     WOp w[NW];
     AOp a[FA];
 };
@@ -899,14 +960,17 @@ __device__ __forceinline__ void skinny_load(const uint8_t* __restrict__ Xq,
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
         const uint8_t* wblk = Wq + ((size_t)(nb0 + i) * kblocks + j) * F::kWBlock;
-        if constexpr (FMT == kFmtF6) op.w[i] = load_f6_operand(wblk, lane);
+        if constexpr (fp6_fmt(FMT)) op.w[i] = load_f6_operand(wblk, lane);
         else op.w[i] = *reinterpret_cast<const uint2*>(wblk + lane * 8);
     }
 #pragma unroll
     for (int g = 0; g < FA; ++g) {
         if (g < mb) {
             const uint8_t* ablk = Xq + ((size_t)g * kblocks + j) * F::kABlock;
-            if constexpr (FMT == kFmtF6) op.a[g] = load_f6_operand(ablk, lane);
+            if constexpr (FMT == kFmtD6) {
+                op.a[g].p[0] = load_f6_operand(ablk, lane);
+                op.a[g].p[1] = load_f6_operand(ablk + Fmt<kFmtD6>::kPlaneBytes, lane);
+            } else if constexpr (FMT == kFmtF6) op.a[g] = load_f6_operand(ablk, lane);
             else if constexpr (FMT == kFmtA8) op.a[g] = *reinterpret_cast<const uint4*>(ablk + lane * 16);
             else op.a[g] = *reinterpret_cast<const uint2*>(ablk + lane * 8);
         }
@@ -918,7 +982,19 @@ __device__ __forceinline__ void skinny_mma(const SkinnyOps<FMT, FA, NW>& op, int
                                            typename Fmt<FMT>::Acc (&acc)[NW][FA]) {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-        if constexpr (FMT == kFmtF6) {
+        if constexpr (FMT == kFmtD6) {
+            using F = Fmt<kFmtD6>;
+#pragma unroll
+            for (int g = 0; g < FA; ++g)
+                if (g < mb) {
+                    acc[i][g] = mfma_scale_f32_32x32x64_fp6(
+                        op.w[i], op.a[g].p[0], acc[i][g], 2, 2, F::kWeightScaleSel,
+                        F::kScaleWord, F::plane_scale_sel(0), F::kScaleWord);
+                    acc[i][g] = mfma_scale_f32_32x32x64_fp6(
+                        op.w[i], op.a[g].p[1], acc[i][g], 2, 2, F::kWeightScaleSel,
+                        F::kScaleWord, F::plane_scale_sel(1), F::kScaleWord);
+                }
+        } else if constexpr (FMT == kFmtF6) {
 #pragma unroll
             for (int g = 0; g < FA; ++g)
                 if (g < mb)
@@ -946,8 +1022,9 @@ __device__ __forceinline__ void skinny_mma(const SkinnyOps<FMT, FA, NW>& op, int
 // operand buffers within ~200 registers with them.
 template <int FMT, int FA, int NW>
 struct SkinnyChunk {
-    static constexpr int kRegs = NW * (FMT == kFmtF6 ? 6 : 2) +
-                                 FA * (FMT == kFmtF6 ? 6 : (FMT == kFmtA8 ? 4 : 2));
+    static constexpr int kRegs =
+        NW * (fp6_fmt(FMT) ? 6 : 2) +
+        FA * (FMT == kFmtD6 ? 12 : FMT == kFmtF6 ? 6 : (FMT == kFmtA8 ? 4 : 2));
     static constexpr int kFit = (200 - 16 * NW * FA) / (2 * kRegs);
     static constexpr int D = NW == 1 ? (kRegs <= 12 ? 8 : (kRegs <= 24 ? 4 : 2))
                                      : (kFit >= 8 ? 8 : kFit >= 4 ? 4 : kFit >= 2 ? 2 : 1);
@@ -1109,7 +1186,7 @@ __device__ __forceinline__ void skinny_tile(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int w = sum[m * kPitch + c * 8 + i];
-            if constexpr (FMT == kFmtF6) v[i] = w;
+            if constexpr (fp6_fmt(FMT)) v[i] = w;
             else if constexpr (FMT == kFmtA8) v[i] = w >> 4;
             else v[i] = w >> 8;
             y[i] = __builtin_fmaf(a[i], (float)v[i] * (rs * ws[i]), b[i]);
@@ -1188,7 +1265,7 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (attr != hipSuccess) return attr;
     const int tiles_n = (N + BN - 1) / BN;
-    const bool split = EPI == kEpiBf16 && FMT != kFmtF6 && split_m > 0 && split_m < M &&
+    const bool split = EPI == kEpiBf16 && !fp6_fmt(FMT) && split_m > 0 && split_m < M &&
                        split_m % BM == 0;
     const bool tail = EPI == kEpiBf16 && !split && tail_m0 > 0 && tail_m0 < M &&
                       tail_m0 % BM == 0 && M - tail_m0 <= kSkinnyMaxM;
@@ -1232,12 +1309,19 @@ hipError_t launch_small(const uint8_t* xq, const float* row_scale, const uint8_t
                         int32_t* acc_out, hipStream_t stream) {
     // 64-row groups for few rows, and when several 128-row groups would
     // still leave compute units idle (the 192-row remainder of a 2048-wide
-    // layer: 128 workgroups of 128 rows, 192 of 64)
-    if (M <= 64 || (M > 128 && (N / 32) * ((M + 127) / 128) < device_cus()))
+    // layer: 128 workgroups of 128 rows, 192 of 64); always for the digit
+    // format, whose two activation planes per fragment leave no registers
+    // for 128-row groups
+    if constexpr (FMT == kFmtD6) {
         return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
                                               M, N, K, S, Y, acc_out, stream);
-    return launch_skinny<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
-                                          N, K, S, Y, acc_out, stream);
+    } else {
+        if (M <= 64 || (M > 128 && (N / 32) * ((M + 127) / 128) < device_cus()))
+            return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
+                                                  comp_b, M, N, K, S, Y, acc_out, stream);
+        return launch_skinny<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
+                                              M, N, K, S, Y, acc_out, stream);
+    }
 }
 
 // The tiled kernel's LDS ring holds two stages of activation codes.
@@ -1292,7 +1376,7 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
                                               m_main);
         // wider layers, int containers: the remainder as half-width tiles in
         // the same launch
-        if (FMT != kFmtF6 && m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && N >= BN)
+        if (!fp6_fmt(FMT) && m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && N >= BN)
             return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
                                               N, K, S, Y, acc_out, stream, NextLayerQuant{},
                                               m_main);
@@ -1313,6 +1397,7 @@ hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* 
                                            N, K, S, Y, acc_out, stream)                       \
                    : launch_fmt<FMT, false>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,  \
                                             M, N, K, S, Y, acc_out, stream)
+    if (codes == RUDDER_CODES_E2M3 && abits == 8) RUDDER_LAUNCH(kFmtD6);
     if (codes == RUDDER_CODES_E2M3) RUDDER_LAUNCH(kFmtF6);
     if (abits == 8) RUDDER_LAUNCH(kFmtA8);
     RUDDER_LAUNCH(kFmtA4);
@@ -1367,6 +1452,8 @@ hipError_t launch_linear_gelu_quant(const void* Xq, const float* row_scale, cons
                                     const float* comp_b, int M, int N, int K, int S, int abits,
                                     int codes, const NextLayerQuant& next, hipStream_t stream) {
     const uint8_t* xq = static_cast<const uint8_t*>(Xq);
+    // (8-bit codes in the E2M3 container are not built for this path)
+    if (codes == RUDDER_CODES_E2M3 && abits == 8) return hipErrorInvalidValue;
     if (codes == RUDDER_CODES_E2M3)
         return launch_fused_fmt<kFmtF6>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
                                         S, next, stream);

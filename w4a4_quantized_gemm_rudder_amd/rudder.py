@@ -25,7 +25,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "_lib", "librudder.so")
 
 CODES_INT = 0       # int4 split-nibble / int8 codes (int8 matrix cores)
-CODES_E2M3 = 1      # 4-bit codes held as FP6 E2M3 (W4A4; f8f6f4 matrix cores)
+CODES_E2M3 = 1      # codes held as FP6 E2M3 (8-bit codes as two digit planes); f8f6f4 MFMA
 
 RUDDER_OK = 0
 RUDDER_ERR_INVALID_ARG = 1

@@ -176,6 +176,11 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     (8292, 384, 4096, 4, 4, False, 49, CODES_E2M3),
     (8292, 128, 2048, 3, 8, False, 56, CODES_E2M3),     # 8-bit codes as digit planes
     (8384, 256, 2048, 3, 8, True, 57, CODES_E2M3),
+    # a remainder of exactly 256 rows (the largest streamed: four 64-row
+    # groups), and 257 rows (not streamed: a partial round of full tiles)
+    (8448, 128, 2048, 3, 8, False, 58, CODES_INT),
+    (8448, 256, 2048, 2, 4, True, 59, CODES_E2M3),
+    (8449, 128, 2048, 3, 4, False, 60, CODES_INT),
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")

@@ -843,19 +843,18 @@ __device__ __forceinline__ void skinny_tile(
 // were last read a whole step earlier) these loads bring them into the
 // memory-side cache ahead of the tiles' own reads.
 // The other blocks, numbered from 0: [0, narrow_first) are BM x BN tiles of
-// rows 0 .. tiles_m * BM - 1 in the XCD-aware order; blocks from
-// narrow_first on (int containers, bf16 output) cover rows narrow_m0 .. M - 1
-// in tiles of BN / 2 channels; blocks from tail_first on (bf16 output)
-// cover rows tail_m0 .. M - 1 of a narrow layer as streaming blocks of 64
-// rows x 32 channels (the weight-streaming kernel's work, four waves
-// splitting k), which the compute units pick up as the last round of tiles
-// drains.  A
-// ragged last round of a wide layer (a few rows past a whole number of
-// rounds) thus runs as twice as many half-width tiles, each about half as
-// long on these MFMA-bound formats, which the compute units pick up as the
-// full-width tiles of the previous round drain.  (An E2M3 tile is bound by
-// its operand stream, and a half-width one still reads the whole
-// activation panel: no gain there.)
+// rows 0 .. tiles_m * BM - 1 in the XCD-aware order.  The rows past the last
+// whole round of tiles, when there are a few, take one of two forms after
+// them in the same launch, which the compute units pick up as the full
+// tiles drain:
+//   - narrow layers (bf16 output): blocks from tail_first on cover rows
+//     tail_m0 .. M - 1 as streaming blocks of 64 rows x 32 channels (the
+//     weight-streaming kernel's work, its four waves splitting k);
+//   - wider layers, int containers (bf16 output): blocks from narrow_first
+//     on cover rows narrow_m0 .. M - 1 as tiles of BN / 2 channels, twice as
+//     many and each about half as long on these MFMA-bound formats.  (An
+//     E2M3 tile is bound by its operand stream, and a half-width one still
+//     reads the whole activation panel: no gain there.)
 template <int FMT, int NS, bool ACC_OUT, int EPI>
 __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const uint8_t* __restrict__ Xq, const float* __restrict__ row_scale,

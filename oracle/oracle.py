@@ -157,8 +157,10 @@ def quant_act(X: np.ndarray, stream_id: np.ndarray, inv_s: np.ndarray, delta: np
 
 
 def pack_int4(codes: np.ndarray) -> np.ndarray:
-    """int8 codes [R, K] -> split-nibble words uint8 [R, K/2].
-    Pinned by: a hand-written byte fixture in tests/golden and round trip."""
+    """int8 codes [R, K] -> uint8 [R, K/2], two codes per byte (code 2i in
+    the low nibble of byte i, code 2i+1 in the high nibble).  A storage
+    format only: parity compares unpacked codes.  Pinned by: a hand-derived
+    byte fixture in tests/golden, one-code placement, round trip."""
     codes = _c(codes, np.int8)
     R, K = codes.shape
     out = np.empty((R, K // 2), np.uint8)

@@ -36,10 +36,9 @@
  * written) operation with round-to-nearest-even; the file is compiled with
  * -ffp-contract=off so no multiply-add is fused unless fmaf() is called.
  *
- * Packed 4-bit codes use "split-nibble words": each group of 8 consecutive
- * k (starting at a multiple of 8) is one little-endian 32-bit word; byte j
- * (j = 0..3) holds code k0+j in bits 0..3 and code k0+4+j in bits 4..7, as
- * two's-complement nibbles.
+ * Packed 4-bit codes (a storage format, not part of the arithmetic): two
+ * codes per byte along k, byte i of a row holding code 2i in bits 0..3 and
+ * code 2i+1 in bits 4..7, as two's-complement nibbles.
  */
 #include <math.h>
 #include <stdint.h>
@@ -188,36 +187,33 @@ int oracle_quant_act(const uint16_t* X, const uint8_t* stream_id, const float* i
 
 /* ---- packing ------------------------------------------------------------ */
 
-/* codes int8 [R][K] in [-8, 7] -> split-nibble words uint8 [R][K/2]; K % 8 == 0. */
+/* codes int8 [R][K] in [-8, 7] -> uint8 [R][K/2], two codes per byte:
+ * byte i = (code 2i & 0xF) | (code 2i+1 & 0xF) << 4; K even. */
 int oracle_pack_int4(const int8_t* codes, long R, int K, uint8_t* packed) {
-    if (K % 8) return ORACLE_BAD_INPUT;
+    if (K % 2) return ORACLE_BAD_INPUT;
     for (long r = 0; r < R; ++r) {
         const int8_t* c = codes + r * K;
         uint8_t* p = packed + r * (K / 2);
-        for (int g = 0; g < K / 8; ++g) {
-            for (int j = 0; j < 4; ++j) {
-                uint8_t lo = (uint8_t)(c[8 * g + j] & 0xF);
-                uint8_t hi = (uint8_t)(c[8 * g + 4 + j] & 0xF);
-                p[4 * g + j] = (uint8_t)(lo | (hi << 4));
-            }
+        for (int i = 0; i < K / 2; ++i) {
+            uint8_t lo = (uint8_t)(c[2 * i] & 0xF);
+            uint8_t hi = (uint8_t)(c[2 * i + 1] & 0xF);
+            p[i] = (uint8_t)(lo | (hi << 4));
         }
     }
     return ORACLE_OK;
 }
 
-/* split-nibble words uint8 [R][K/2] -> int8 codes [R][K] (sign-extended). */
+/* uint8 [R][K/2] two codes per byte -> int8 codes [R][K] (sign-extended). */
 int oracle_unpack_int4(const uint8_t* packed, long R, int K, int8_t* codes) {
-    if (K % 8) return ORACLE_BAD_INPUT;
+    if (K % 2) return ORACLE_BAD_INPUT;
     for (long r = 0; r < R; ++r) {
         const uint8_t* p = packed + r * (K / 2);
         int8_t* c = codes + r * K;
-        for (int g = 0; g < K / 8; ++g) {
-            for (int j = 0; j < 4; ++j) {
-                int lo = p[4 * g + j] & 0xF;
-                int hi = (p[4 * g + j] >> 4) & 0xF;
-                c[8 * g + j] = (int8_t)(lo >= 8 ? lo - 16 : lo);
-                c[8 * g + 4 + j] = (int8_t)(hi >= 8 ? hi - 16 : hi);
-            }
+        for (int i = 0; i < K / 2; ++i) {
+            int lo = p[i] & 0xF;
+            int hi = (p[i] >> 4) & 0xF;
+            c[2 * i] = (int8_t)(lo >= 8 ? lo - 16 : lo);
+            c[2 * i + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
         }
     }
     return ORACLE_OK;

@@ -305,6 +305,195 @@ def test_epilogue_fp64_bound(orc):
     assert np.all(np.abs(Y - ref) <= bound)
 
 
+# Exact-rational reference of the epilogue ("SteerQuant" digest §4.4:
+# dequantization, then inverse-gain compensation and bias; the compensation
+# is one fp32 multiply-add).  Every value is held as an exact rational
+# (integer numerator, power-of-two denominator) and rounded to fp32 only where
+# the stated arithmetic rounds:
+#   d = RNE32(rs * ws);  t = RNE32(f * d);  y = RNE32(a * t + b)  (one rounding)
+# then Y = bf16 RNE (torch's cast).  Nothing here calls the oracle.
+
+def _ratio(x):
+    """fp32/fp64 value -> (numerator, denominator) exactly."""
+    return float(x).as_integer_ratio()
+
+
+def _rne_f32(num, den):
+    """Round num/den (den a power of two) to the nearest fp32, ties to even
+    (normal range; the epilogue's values never leave it)."""
+    if num == 0:
+        return 0.0
+    neg = num < 0
+    mag = -num if neg else num
+    # scale so that the quotient has 24 bits before the point
+    sh = 24 - (mag.bit_length() - (den.bit_length() - 1))
+    # value * 2^sh has its leading bit at position 23 or 24
+    q_num = mag << sh if sh >= 0 else mag
+    q_den = den if sh >= 0 else den << (-sh)
+    q, r = divmod(q_num, q_den)
+    if q >= 1 << 24:                       # leading bit landed at 24: one less bit
+        sh -= 1
+        q_num = mag << sh if sh >= 0 else mag
+        q_den = den if sh >= 0 else den << (-sh)
+        q, r = divmod(q_num, q_den)
+    assert (1 << 23) <= q < (1 << 24)
+    if 2 * r > q_den or (2 * r == q_den and (q & 1)):
+        q += 1
+    val = float(q) * 2.0 ** (-sh)
+    assert np.isfinite(val) and abs(val) >= 2.0 ** -126
+    return -val if neg else val
+
+
+def _mul_exact(x, y):
+    (n1, d1), (n2, d2) = _ratio(x), _ratio(y)
+    return n1 * n2, d1 * d2
+
+
+def _fma_exact(a, t, b):
+    n1, d1 = _mul_exact(a, t)
+    n2, d2 = _ratio(b)
+    d = max(d1, d2)
+    return n1 * (d // d1) + n2 * (d // d2), d
+
+
+def _epilogue_ref(f, rs, ws, a, b, form="fused"):
+    """fp32 y of one output element.  form: "fused" (the stated arithmetic),
+    "unfused" (a * t rounded before + b) or "reassoc" ((f * rs) * ws)."""
+    if form == "reassoc":
+        t = _rne_f32(*_mul_exact(_rne_f32(*_mul_exact(f, rs)), ws))
+    else:
+        t = _rne_f32(*_mul_exact(f, _rne_f32(*_mul_exact(rs, ws))))
+    if form == "unfused":
+        p = _rne_f32(*_mul_exact(a, t))
+        n1, d1 = _ratio(p)
+        n2, d2 = _ratio(b)
+        d = max(d1, d2)
+        return _rne_f32(n1 * (d // d1) + n2 * (d // d2), d)
+    return _rne_f32(*_fma_exact(a, t, b))
+
+
+def _bf16_of(y):
+    return int(torch_bf16_bits(np.asarray([y], np.float32))[0])
+
+
+def test_exact_rational_reference_selfcheck():
+    """The rational rounding helper agrees with the correctly rounded fp64 ->
+    fp32 conversion wherever fp64 holds the value exactly (products of two
+    fp32 values), including constructed ties."""
+    rng = np.random.default_rng(40)
+    x = rng.uniform(-1e3, 1e3, 4000).astype(np.float32)
+    y = rng.uniform(-1e-2, 1e-2, 4000).astype(np.float32)
+    prod = x.astype(np.float64) * y.astype(np.float64)          # exact in fp64
+    want = prod.astype(np.float32)
+    got = np.array([_rne_f32(*_mul_exact(u, v)) for u, v in zip(x, y)], np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # ties: 1 + 2^-24 -> 1 (even), 1 + 3 * 2^-24 -> 1 + 2^-22 (even), and negatives
+    for num, den, v in (((1 << 24) + 1, 1 << 24, 1.0),
+                        ((1 << 24) + 3, 1 << 24, 1.0 + 2.0 ** -22),
+                        (-((1 << 24) + 1), 1 << 24, -1.0)):
+        assert _rne_f32(num, den) == v
+
+
+def _epilogue_random_inputs(rng, M, N, S):
+    acc = rng.integers(-2 * 10**6, 2 * 10**6, (M, N)).astype(np.int32)
+    acc[rng.random((M, N)) < 0.05] = 0
+    sid = rng.integers(0, S, M).astype(np.uint8)
+    rs = rng.uniform(1e-4, 1e-1, M).astype(np.float32)
+    ws = rng.uniform(1e-5, 1e-2, N).astype(np.float32)
+    a = rng.uniform(0.9, 1.1, (S, N)).astype(np.float32)
+    b = (rng.standard_normal((S, N)) * rng.choice([1e-3, 1e-2, 1.0], (S, N))).astype(np.float32)
+    return acc, sid, rs, ws, a, b
+
+
+def test_epilogue_exact_rational_random(orc):
+    """Over 10^5 random outputs the oracle equals the exact-rational
+    reference bit for bit."""
+    rng = np.random.default_rng(41)
+    M, N, S = 400, 256, 3
+    acc, sid, rs, ws, a, b = _epilogue_random_inputs(rng, M, N, S)
+    Y = orc.epilogue(acc, rs, sid, ws, a, b)
+    y = np.empty((M, N), np.float64)
+    for m in range(M):
+        s = sid[m]
+        for n in range(N):
+            y[m, n] = _epilogue_ref(int(acc[m, n]), rs[m], ws[n], a[s, n], b[s, n])
+    assert np.array_equal(Y, torch_bf16_bits(y.astype(np.float32)))
+
+
+def _constructed_fma_cases(rng, count):
+    """Cancellation cases: b = -RNE32(a*t) + k*ulp32(a*t) for a small k, so
+    that the exact a*t + b is k*ulp minus the low bits of the exact product.
+    Rounding a*t before adding b drops exactly those bits (the unfused form
+    gives k*ulp), the single-rounding form keeps them."""
+    cases = []
+    while len(cases) < count:
+        f = int(rng.integers(1, 1 << 21))
+        rs = np.float32(rng.uniform(1e-3, 1e-1))
+        ws = np.float32(rng.uniform(1e-4, 1e-2))
+        a = np.float32(rng.uniform(0.9, 1.1))
+        t = _rne_f32(*_mul_exact(f, _rne_f32(*_mul_exact(rs, ws))))
+        p32 = _rne_f32(*_mul_exact(a, t))
+        ulp = 2.0 ** (np.floor(np.log2(abs(p32))) - 23)
+        k = int(rng.integers(-3, 4))
+        b = np.float32(-p32 + k * ulp)
+        assert float(b) == -p32 + k * ulp               # exact by construction
+        cases.append((f, rs, ws, a, b))
+    return cases
+
+
+def _constructed_assoc_cases(rng, count):
+    """f * rs * ws placed on a bf16 rounding midpoint (9 significant bits),
+    so that the one-ulp difference between RNE32(f * RNE32(rs * ws)) and
+    RNE32(RNE32(f * rs) * ws) can decide the bf16 output (a = 1, b = 0)."""
+    cases = []
+    while len(cases) < count:
+        f = int(rng.integers(1, 1 << 21))
+        rs = np.float32(rng.uniform(1e-3, 1e-1))
+        e = int(rng.integers(-12, -2))
+        mid = (int(rng.integers(128, 256)) + 0.5) * 2.0 ** e
+        ws = np.float32(mid / (f * float(rs)))
+        cases.append((f, rs, ws, np.float32(1.0), np.float32(0.0)))
+    return cases
+
+
+def _discriminating(cases, other):
+    keep = []
+    for c in cases:
+        ref = _bf16_of(_epilogue_ref(*c))
+        alt = _bf16_of(_epilogue_ref(*c, form=other))
+        if ref != alt:
+            keep.append(c)
+    return keep
+
+
+@pytest.mark.parametrize("other,make", [("unfused", _constructed_fma_cases),
+                                        ("reassoc", _constructed_assoc_cases)])
+def test_epilogue_form_and_order_pinned(orc, other, make):
+    """Constructed cases on which the single-rounding fma form (resp. the
+    order f * (rs * ws)) and the plausible alternative -- a * t rounded
+    before adding b, resp. (f * rs) * ws -- give different bf16 outputs.  The
+    oracle must give the stated form's output on every one of them, so either
+    mistake fails this test."""
+    rng = np.random.default_rng(42 if other == "unfused" else 43)
+    cases = _discriminating(make(rng, 6000), other)
+    assert len(cases) >= 500, f"only {len(cases)} discriminating cases"
+    cases = cases[:1000]
+    # one call: case i is row i (its own step size and stream) and channel i
+    # (its own channel scale and compensation); only the diagonal is used
+    n = len(cases)
+    acc = np.zeros((n, n), np.int32)
+    acc[np.arange(n), np.arange(n)] = [c[0] for c in cases]
+    rs = np.array([c[1] for c in cases], np.float32)
+    ws = np.array([c[2] for c in cases], np.float32)
+    a = np.array([[c[3] for c in cases]], np.float32)
+    b = np.array([[c[4] for c in cases]], np.float32)
+    Y = np.diagonal(orc.epilogue(acc, rs, np.zeros(n, np.uint8), ws, a, b)).copy()
+    want = np.array([_bf16_of(_epilogue_ref(*c)) for c in cases], np.uint16)
+    alt = np.array([_bf16_of(_epilogue_ref(*c, form=other)) for c in cases], np.uint16)
+    assert np.array_equal(Y, want)
+    assert not np.any(Y == alt)
+
+
 # ---------------------------------------------------------------------------
 # Whole chain
 # ---------------------------------------------------------------------------
@@ -443,7 +632,7 @@ def test_non_finite_rejected(orc):
 # ---------------------------------------------------------------------------
 
 def _golden_pack_rows():
-    path = os.path.join(ROOT, "tests", "golden", "pack_int4_split_nibble.txt")
+    path = os.path.join(ROOT, "tests", "golden", "pack_int4_pairs.txt")
     rows = []
     for line in open(path):
         line = line.strip()
@@ -467,6 +656,20 @@ def test_pack_roundtrip_random(orc):
     rng = np.random.default_rng(12)
     c = rng.integers(-8, 8, (33, 256)).astype(np.int8)
     assert np.array_equal(orc.unpack_int4(orc.pack_int4(c), 256), c)
+
+
+def test_pack_nibble_positions(orc):
+    """Each code lands in the nibble its index names: code k of a row is
+    nibble k % 2 of byte k // 2 (placed one at a time, all others zero)."""
+    K = 16
+    for k in range(K):
+        for v in (-8, -1, 1, 7):
+            c = np.zeros((1, K), np.int8)
+            c[0, k] = v
+            got = orc.pack_int4(c)[0]
+            want = np.zeros(K // 2, np.uint8)
+            want[k // 2] = (v & 0xF) << (4 * (k % 2))
+            assert np.array_equal(got, want), (k, v)
 
 
 # ---------------------------------------------------------------------------

@@ -279,6 +279,18 @@ rudder_status_t rudder_linear_gelu_quant(const void* Xq, const float* row_scale,
 rudder_status_t rudder_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, void* stream);
 
 /*
+ * Calibration support (SteerQuant App. C.1: the activation-error target uses
+ * unquantized activations and the fixed quantized weights).  Unpacks Wq
+ * (either container) into out[k][n] = fl32(qw[k][n] * w_scale[n]), fp32
+ * [K][N] row-major.  K, N as for rudder_quantize_weights.
+ * Errors: INVALID_ARG for a null pointer, K or N <= 0 or not a multiple of 32
+ * (K of 64 for E2M3), an unknown container.
+ */
+rudder_status_t rudder_dequant_weights(const uint8_t* Wq, const float* w_scale, int K, int N,
+                                       int codes, float* out, void* stream);
+
+
+/*
  * Calibration support (SteerQuant §4.2, §4.3, App. C: the shared diagonal and
  * the layer-step thresholds and stream gains are chosen offline by a
  * map-weighted reconstruction error whose weights differ per stream).
@@ -294,17 +306,6 @@ rudder_status_t rudder_gelu_bf16(const uint16_t* in, uint16_t* out, size_t n, vo
  *   M >= 0 (M = 0 writes sse = 0), N > 0, 1 <= S <= 8
  * Errors: INVALID_ARG for a null pointer, M < 0, N <= 0, S outside 1..8.
  */
-/*
- * Calibration support (SteerQuant App. C.1: the activation-error target uses
- * unquantized activations and the fixed quantized weights).  Unpacks Wq
- * (either container) into out[k][n] = fl32(qw[k][n] * w_scale[n]), fp32
- * [K][N] row-major.  K, N as for rudder_quantize_weights.
- * Errors: INVALID_ARG for a null pointer, K or N <= 0 or not a multiple of 32
- * (K of 64 for E2M3), an unknown container.
- */
-rudder_status_t rudder_dequant_weights(const uint8_t* Wq, const float* w_scale, int K, int N,
-                                       int codes, float* out, void* stream);
-
 size_t rudder_stream_sq_error_workspace_bytes(void);
 rudder_status_t rudder_stream_sq_error(const uint16_t* Y, const float* Yref,
                                        const uint8_t* stream_id, int M, int N, int S,

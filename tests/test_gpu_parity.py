@@ -316,46 +316,121 @@ def test_m0_is_noop_on_device():
 
 
 # ---------------------------------------------------------------------------
-# Full-size workloads (the launch configuration the benchmark times): codes
-# and row scales compared in full, accumulators and outputs on sampled rows.
+# Full-size workloads (the launch configuration the benchmark times), in
+# every code container the benchmark can run them in.  Codes and row scales
+# are compared in full at every step listed; accumulators and outputs on
+# every row at the "full" steps, and on sampled rows (first/last rows, every
+# stream boundary, the ragged tail, random rows) at the others.  The two
+# containers of one layer are adjacent and share their full step, so the
+# oracle runs once for both.
 # ---------------------------------------------------------------------------
 
+_C2, _C3 = "attn_proj_h2048_m4192_w4a8", "mlp_h2048_m4192_w4a4"
+_C4, _C5 = "dit_block_h2048_m8384_16step", "backbone_h4096_m16576_w4a4"
 FULL = [
-    ("attn_proj_h2048_m4192_w4a8", "qkv", None, CODES_INT),
-    ("attn_proj_h2048_m4192_w4a8", "o", None, CODES_INT),
-    ("mlp_h2048_m4192_w4a4", "up", None, CODES_INT),
-    ("mlp_h2048_m4192_w4a4", "down", None, CODES_INT),
-    ("mlp_h2048_m4192_w4a4", "up", [0], CODES_E2M3),
-    ("mlp_h2048_m4192_w4a4", "down", [0], CODES_E2M3),
-    ("dit_block_h2048_m8384_16step", "qkv", [0, 15], CODES_INT),
-    ("dit_block_h2048_m8384_16step", "o", [3], CODES_INT),
-    ("dit_block_h2048_m8384_16step", "up", [7], CODES_INT),
-    ("dit_block_h2048_m8384_16step", "down", [0, 11, 15], CODES_INT),
-    ("dit_block_h2048_m8384_16step", "up", [2], CODES_E2M3),
-    ("dit_block_h2048_m8384_16step", "down", [9, 15], CODES_E2M3),
-    ("dit_block_h2048_m8384_16step", "qkv", [0], CODES_E2M3),
-    ("dit_block_h2048_m8384_16step", "o", [6], CODES_E2M3),
-    ("backbone_h4096_m16576_w4a4", "qkv", [0], CODES_INT),
-    ("backbone_h4096_m16576_w4a4", "o", [19], CODES_INT),
-    ("backbone_h4096_m16576_w4a4", "up", [4], CODES_INT),
-    ("backbone_h4096_m16576_w4a4", "down", [13], CODES_INT),
-    ("backbone_h4096_m16576_w4a4", "qkv", [5], CODES_E2M3),
-    ("backbone_h4096_m16576_w4a4", "down", [8], CODES_E2M3),
+    # workload, layer, codes, steps with every row, steps with sampled rows
+    (_C2, "qkv", CODES_INT, [0], list(range(1, 10))),
+    (_C2, "qkv", CODES_E2M3, [0], [9]),
+    (_C2, "o", CODES_INT, [0], list(range(1, 10))),
+    (_C2, "o", CODES_E2M3, [0], [4]),
+    (_C3, "up", CODES_E2M3, [0], list(range(1, 10))),
+    (_C3, "up", CODES_INT, [0], [6]),
+    (_C3, "down", CODES_E2M3, [0], list(range(1, 10))),
+    (_C3, "down", CODES_INT, [0], [3]),
+    (_C4, "qkv", CODES_INT, [0], [15]),
+    (_C4, "qkv", CODES_E2M3, [0], []),
+    (_C4, "o", CODES_INT, [3], [12]),
+    (_C4, "o", CODES_E2M3, [3], []),
+    (_C4, "up", CODES_E2M3, [2], [7]),
+    (_C4, "up", CODES_INT, [2], []),
+    (_C4, "down", CODES_E2M3, [9], [15]),
+    (_C4, "down", CODES_INT, [9], [0, 11]),
+    (_C5, "qkv", CODES_E2M3, [5], [19]),
+    (_C5, "qkv", CODES_INT, [5], []),
+    (_C5, "o", CODES_E2M3, [19], [0]),
+    (_C5, "o", CODES_INT, [19], []),
+    (_C5, "up", CODES_E2M3, [4], [11]),
+    (_C5, "up", CODES_INT, [4], []),
+    (_C5, "down", CODES_E2M3, [13], [8]),
+    (_C5, "down", CODES_INT, [13], []),
 ]
+
+# the inputs of the last (workload, layer), shared by its containers
+_INPUTS: dict = {}
+
+
+def _layer_inputs(workload, layer):
+    from w4a4_quantized_gemm_rudder_amd import workloads as W
+    key = (workload, layer)
+    if _INPUTS.get("key") != key:
+        _INPUTS.clear()
+        _INPUTS.update(key=key, val=W.make_inputs(workload, seed=0, layers=[layer]))
+    return _INPUTS["val"]
 
 
 @pytest.mark.slow
-@pytest.mark.parametrize("workload,layer,steps,codes", FULL)
-def test_full_size_layer(workload, layer, steps, codes):
-    from w4a4_quantized_gemm_rudder_amd import workloads as W
-    log(f"case full {workload}/{layer} steps={steps} codes={codes}")
-    wi = W.make_inputs(workload, seed=0, layers=[layer])
+@pytest.mark.parametrize("workload,layer,codes,full_steps,sampled_steps", FULL)
+def test_full_size_layer(workload, layer, codes, full_steps, sampled_steps):
+    log(f"case full {workload}/{layer} codes={codes} every row at steps {full_steps}, "
+        f"sampled rows at steps {sampled_steps}")
+    wi = _layer_inputs(workload, layer)
     L = wi.layers[0]
     run = LayerRun(L.x, wi.stream_id, L.w, L.smooth, L.comp_a, L.comp_b, 3, L.layer.abits,
                    codes)
     run.check_weights()
     rows = sample_rows(wi.stream_id, seed=len(layer))
-    for t in (steps if steps is not None else range(wi.workload.n_steps)):
+    for t in full_steps:
+        a, b = L.step_comp(t)
+        st = run.run_step(L.act_scale[t], a, b, rows=None, label=f"{workload}/{layer}/t{t}",
+                          oracle_key=(workload, layer, t))
+        log(f"  step {t} (every row): {st}")
+    for t in sampled_steps:
         a, b = L.step_comp(t)
         st = run.run_step(L.act_scale[t], a, b, rows=rows, label=f"{workload}/{layer}/t{t}")
         log(f"  step {t}: {st}")
+    del run
+
+
+# ---------------------------------------------------------------------------
+# Round-half-to-even ties on the GPU: activations and weights constructed so
+# that the scaled value of many elements is exactly k + 1/2 (power-of-two
+# step sizes and channel scales, unit smoothing), in every container.
+# ---------------------------------------------------------------------------
+
+def _tie_inputs(abits, M=96, K=256, N=64, seed=0):
+    rng = np.random.default_rng(300 + seed)
+    qa = 127 if abits == 8 else 7
+    S = 2
+    sid = (np.arange(M) % S).astype(np.uint8)
+    delta = np.array([0.25, 1.0], np.float32)                  # exact reciprocals
+    # activations: half-integers k + 1/2 (k up to Qa, so +-(Qa + 1/2) clamps),
+    # mixed with integers and random values
+    half = rng.integers(-qa - 1, qa + 1, (M, K)) + 0.5
+    v = np.where(rng.random((M, K)) < 0.7, half, rng.uniform(-qa - 3, qa + 3, (M, K)))
+    x = v * delta[sid][:, None].astype(np.float64)
+    X = _torch_bf16_bits(x)
+    xv = (np.asarray(X, np.uint32) << 16).view(np.float32)
+    assert np.mean(np.abs(xv / delta[sid][:, None] % 1.0 - 0.5) == 0) > 0.5  # real ties
+    # weights: column n has scale 2^e_n (one entry +-7 * 2^e_n sets the column
+    # absmax), the others are half-integer multiples of 2^e_n
+    e = rng.integers(-9, -5, N)
+    wq = rng.integers(-7, 7, (K, N)) + 0.5
+    wq[rng.integers(0, K, N), np.arange(N)] = 7.0 * np.where(rng.random(N) < 0.5, -1, 1)
+    Wb = _torch_bf16_bits(wq * 2.0 ** e[None, :])
+    s = np.ones(K, np.float32)
+    a = rng.uniform(0.9, 1.1, (S, N)).astype(np.float32)
+    b = (rng.standard_normal((S, N)) * 0.01).astype(np.float32)
+    return X, sid, Wb, s, a, b, delta, S
+
+
+@pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_INT), (4, CODES_E2M3),
+                                         (8, CODES_E2M3)])
+def test_round_half_even_ties(abits, codes):
+    log(f"case RNE ties abits={abits} codes={codes}")
+    X, sid, Wb, s, a, b, delta, S = _tie_inputs(abits)
+    run = LayerRun(X, sid, Wb, s, a, b, S, abits, codes)
+    run.check_weights()
+    # the oracle's codes hold the ties rounded to even (their values are
+    # pinned on the CPU); here the GPU must produce the same bytes
+    assert np.any(np.abs(run.o_qw) == 2) and np.any(np.abs(run.o_qw) == 6)
+    log(f"  {run.run_step(delta, a, b, label='ties')}")

@@ -62,3 +62,35 @@ def test_step_compensation_shape():
     assert L.comp_a.shape == (16, 3, 2048)
     a, b = L.step_comp(5)
     assert a.shape == (3, 2048)
+
+
+def test_abs_max_from_bit_patterns_matches_values():
+    """Column/row absmax taken on bf16 bit patterns equals the absmax of the
+    values (finite patterns, both signs, zeros, subnormals)."""
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 1 << 16, (700, 96)).astype(np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] &= 0xBFFF          # no inf/NaN exponents
+    vals = np.abs(W.bf16_bits_to_f64(bits))
+    assert np.array_equal(W._abs_max_bits(bits, 0), vals.max(axis=0))
+    assert np.array_equal(W._abs_max_bits(bits, 1), vals.max(axis=1))
+
+
+def test_scales_follow_their_definition():
+    """s_j = sqrt(max|X_j| / max|W_j|) and Delta = rho * max|X diag(s)^-1| /
+    (gamma * Qa), recomputed here directly from the drawn tensors."""
+    wi = W.make_inputs("attn_proj_h2048_m4192_w4a8", rows=700, layers=["qkv"])
+    L = wi.layers[0]
+    x = W.bf16_bits_to_f64(L.x)
+    w = W.bf16_bits_to_f64(L.w)
+    s = np.sqrt(np.abs(x).max(0) / np.abs(w).max(1)).astype(np.float32)
+    assert np.array_equal(s, L.smooth)
+    c0 = (np.abs(x) / L.smooth.astype(np.float64)[None, :]).max()
+    ratio = L.act_scale.astype(np.float64) * 127 / c0       # = rho / gamma
+    assert np.all((ratio > 0.7 / 2 * 0.999) & (ratio < 1.0 / 0.5 * 1.001))
+
+
+def test_block_draws_do_not_depend_on_threads(monkeypatch):
+    a = W.make_inputs("mlp_h2048_m4192_w4a4", rows=1100, layers=["down"]).layers[0].x
+    monkeypatch.setattr(W, "_threads", lambda: 1)
+    b = W.make_inputs("mlp_h2048_m4192_w4a4", rows=1100, layers=["down"]).layers[0].x
+    assert np.array_equal(a, b)

@@ -9,7 +9,9 @@ Workloads are DiT-shaped token sets with three semantic streams
 world-action models in SteerQuant ("SteerQuant: Steering Quantization Error
 with Action-Guided Scaling in World-Action Models", abstract and §1).
 
-Drawing recipe (every draw is fp64, then rounded once):
+Drawing recipe (every draw is fp64, rounded to fp32 and then to bf16, or cast
+to fp32 for scales; large tensors are drawn in blocks of 512 rows, each block
+from its own generator, so that blocks can be drawn in parallel threads):
   * X rows ~ N(0, 1); a fixed number of outlier channels (chosen without
     replacement) are multiplied by a constant factor.
   * The MLP down-projection input is bf16(GELU_erf(Z)), Z ~ Student-t(nu=4).
@@ -30,8 +32,10 @@ rounding is torch's own conversion (input synthesis only).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
-from typing import Dict, List, Optional, Tuple
+import os
+from typing import Callable, Dict, List, Optional, Tuple
 
 import numpy as np
 
@@ -170,33 +174,93 @@ WORKLOAD_ORDER: List[str] = [w.name for w in sorted(WORKLOADS.values(), key=lamb
 # Draws
 # --------------------------------------------------------------------------
 
+# Row-block drawing: each block of _BLOCK_ROWS rows has its own generator
+# (the block index is the last seed word), so blocks are drawn in parallel
+# threads and the result does not depend on the thread count.
+_BLOCK_ROWS = 512
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _draw_blocked(M: int, K: int, fill) -> np.ndarray:
+    """bf16 bits [M, K]; fill(block, rows) returns the fp64 values of row block
+    `block` ([rows, K])."""
+    out = np.empty((M, K), np.uint16)
+    nblk = (M + _BLOCK_ROWS - 1) // _BLOCK_ROWS
+
+    def work(b: int) -> None:
+        r0 = b * _BLOCK_ROWS
+        r1 = min(M, r0 + _BLOCK_ROWS)
+        out[r0:r1] = to_bf16_bits(fill(b, r1 - r0))
+
+    with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(work, range(nblk)))
+    return out
+
+
 def draw_x_normal(M: int, K: int, n_outliers: int, factor: float,
-                  rng_x: np.random.Generator, rng_idx: np.random.Generator) -> np.ndarray:
-    """bf16 bits [M, K]: N(0,1) with n_outliers channels multiplied by factor."""
-    x = rng_x.standard_normal((M, K))
-    if n_outliers:
-        idx = rng_idx.choice(K, size=n_outliers, replace=False)
-        x[:, idx] *= factor
-    return to_bf16_bits(x)
+                  rng_x: Callable[[int], np.random.Generator],
+                  rng_idx: np.random.Generator) -> np.ndarray:
+    """bf16 bits [M, K]: N(0,1) with n_outliers channels multiplied by factor.
+    rng_x(block) gives the generator of a row block."""
+    idx = rng_idx.choice(K, size=n_outliers, replace=False) if n_outliers else None
+
+    def fill(b, rows):
+        x = rng_x(b).standard_normal((rows, K))
+        if idx is not None:
+            x[:, idx] *= factor
+        return x
+
+    return _draw_blocked(M, K, fill)
 
 
-def draw_x_gelu_t4(M: int, K: int, rng: np.random.Generator) -> np.ndarray:
-    """bf16 bits [M, K] of GELU_erf(Z), Z ~ Student-t(4), evaluated in fp64."""
+def draw_x_gelu_t4(M: int, K: int, rng: Callable[[int], np.random.Generator]) -> np.ndarray:
+    """bf16 bits [M, K] of GELU_erf(Z), Z ~ Student-t(4), evaluated in fp64.
+    rng(block) gives the generator of a row block."""
     from scipy.special import erf
-    z = rng.standard_t(4.0, size=(M, K))
-    g = 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
-    return to_bf16_bits(g)
+
+    def fill(b, rows):
+        z = rng(b).standard_t(4.0, size=(rows, K))
+        return 0.5 * z * (1.0 + erf(z / np.sqrt(2.0)))
+
+    return _draw_blocked(M, K, fill)
 
 
-def draw_w(K: int, N: int, sigma: float, rng: np.random.Generator) -> np.ndarray:
-    """bf16 bits [K, N] ~ N(0, sigma)."""
-    return to_bf16_bits(rng.standard_normal((K, N)) * sigma)
+def draw_w(K: int, N: int, sigma: float, rng: Callable[[int], np.random.Generator]) -> np.ndarray:
+    """bf16 bits [K, N] ~ N(0, sigma); rng(block) gives the generator of a
+    block of input-channel rows."""
+    return _draw_blocked(K, N, lambda b, rows: rng(b).standard_normal((rows, N)) * sigma)
 
 
-def smoothing_scale(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+def _abs_max_bits(bits: np.ndarray, axis: int) -> np.ndarray:
+    """max |value| along an axis of finite bf16 bit patterns, as fp64.  The
+    magnitude bits of finite bf16 values order the same way as the values'
+    magnitudes, so the maximum is taken on the patterns (blocks in threads)."""
+    if axis == 0:
+        nblk = (bits.shape[0] + _BLOCK_ROWS - 1) // _BLOCK_ROWS
+
+        def part(b):
+            blk = bits[b * _BLOCK_ROWS:(b + 1) * _BLOCK_ROWS]
+            return (blk & 0x7FFF).max(axis=0)
+
+        with concurrent.futures.ThreadPoolExecutor(_threads()) as ex:
+            m = np.max(np.stack(list(ex.map(part, range(nblk)))), axis=0)
+    else:
+        m = (bits & 0x7FFF).max(axis=1)
+    return bf16_bits_to_f64(m.astype(np.uint16))
+
+
+def smoothing_scale(x_bits: np.ndarray, w_bits: np.ndarray,
+                    x_colmax: Optional[np.ndarray] = None) -> np.ndarray:
     """fp32 [K]: s_j = sqrt(max_m|X_mj| / max_n|W_jn|) in fp64 (1 where a max is 0)."""
-    xm = np.abs(bf16_bits_to_f64(x_bits)).max(axis=0)
-    wm = np.abs(bf16_bits_to_f64(w_bits)).max(axis=1)
+    xm = _abs_max_bits(x_bits, 0) if x_colmax is None else x_colmax
+    wm = _abs_max_bits(w_bits, 1)
     s = np.ones_like(xm)
     ok = (xm > 0) & (wm > 0)
     s[ok] = np.sqrt(xm[ok] / wm[ok])
@@ -204,10 +268,13 @@ def smoothing_scale(x_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
 
 
 def draw_act_scales(x_bits: np.ndarray, s: np.ndarray, n_steps: int, S: int, qa: int,
-                    rng_rho: np.random.Generator, rng_gamma: np.random.Generator) -> np.ndarray:
-    """fp32 [n_steps, S] step sizes Delta = c_t / (gamma_{s,t} * Qa)."""
-    xs = np.abs(bf16_bits_to_f64(x_bits)) / s.astype(np.float64)[None, :]
-    c0 = float(xs.max())
+                    rng_rho: np.random.Generator, rng_gamma: np.random.Generator,
+                    x_colmax: Optional[np.ndarray] = None) -> np.ndarray:
+    """fp32 [n_steps, S] step sizes Delta = c_t / (gamma_{s,t} * Qa), with
+    c_t = rho_t * max_{m,j} |X_mj| / s_j.  Dividing by s_j > 0 is monotonic,
+    so the maximum over m is taken first (the same fp64 value)."""
+    xm = _abs_max_bits(x_bits, 0) if x_colmax is None else x_colmax
+    c0 = float((xm / s.astype(np.float64)).max())
     rho = rng_rho.uniform(0.7, 1.0, size=n_steps)
     gamma = np.exp(rng_gamma.uniform(np.log(0.5), np.log(2.0), size=(n_steps, S)))
     delta = (rho[:, None] * c0) / (gamma * qa)
@@ -266,17 +333,20 @@ def make_inputs(name: str, seed: int = 0, rows: Optional[int] = None,
     wi = wl.index
     tensors: Dict[str, np.ndarray] = {}
 
+    colmax: Dict[str, np.ndarray] = {}
+
     def x_tensor(kind: str, K: int) -> np.ndarray:
         if kind in tensors:
             return tensors[kind]
         if kind == "x2":
-            t = draw_x_gelu_t4(M, K, rng_for(seed, wi, "z", K))
+            t = draw_x_gelu_t4(M, K, lambda b: rng_for(seed, wi, "z", K, b))
         else:
             sub = 0 if kind == "x" else sum(map(ord, kind))
             t = draw_x_normal(M, K, wl.x_outliers[0], wl.x_outliers[1],
-                              rng_for(seed, wi, "x", sub, K),
+                              lambda b: rng_for(seed, wi, "x", sub, K, b),
                               rng_for(seed, wi, "outlier_idx", sub, K))
         tensors[kind] = t
+        colmax[kind] = _abs_max_bits(t, 0)
         return t
 
     out = []
@@ -284,14 +354,15 @@ def make_inputs(name: str, seed: int = 0, rows: Optional[int] = None,
         if layers is not None and layer.name not in layers:
             continue
         x = x_tensor(layer.x_kind, layer.K)
-        w = draw_w(layer.K, layer.N, layer.w_sigma, rng_for(seed, wi, "w", li))
-        s = smoothing_scale(x, w)
+        w = draw_w(layer.K, layer.N, layer.w_sigma, lambda b: rng_for(seed, wi, "w", li, b))
+        s = smoothing_scale(x, w, colmax[layer.x_kind])
         qa = 127 if layer.abits == 8 else 7
         if wl.dynamic:
             delta = None
         else:
             delta = draw_act_scales(x, s, wl.n_steps, wl.S, qa,
-                                    rng_for(seed, wi, "rho", li), rng_for(seed, wi, "gamma", li))
+                                    rng_for(seed, wi, "rho", li), rng_for(seed, wi, "gamma", li),
+                                    colmax[layer.x_kind])
         shape = (wl.n_steps, wl.S, layer.N) if wl.per_step_comp else (wl.S, layer.N)
         a, b = draw_compensation(shape, rng_for(seed, wi, "a", li), rng_for(seed, wi, "b", li))
         out.append(LayerInputs(layer, x, w, s, delta, a, b))
@@ -344,5 +415,5 @@ def make_calibration(K: int, N: int, seed: int = 0, steps: int = 4,
             tags.append(np.full(n, st, np.uint8))
         xs.append(to_bf16_bits(np.concatenate(parts)))
         sids.append(np.concatenate(tags))
-    w = draw_w(K, N, 0.02, rng_for(seed, 100, "w", K, N))
+    w = draw_w(K, N, 0.02, lambda b: rng_for(seed, 100, "w", K, N, b))
     return CalibrationInputs(xs=xs, sids=sids, w=w, scores=CALIB_SCORES[:steps].copy())

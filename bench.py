@@ -15,22 +15,28 @@ seeded synthetic tensors already resident in HBM.
 
 Prints ONE JSON line.  `value` is whole-step throughput in TOPS (2*M*N*K
 summed over the four linears, per second, both kernels of each linear
-included); `us_per_step` is the latency of one step, timed over K steps with
-nothing but the step's launches on the stream, after W untimed steps (the
-default W, ~40 ms of steps, lets the clocks settle to their steady state
-under sustained load, as in a running denoising loop).  The same K steps then run
-again with a HIP event pair around every GEMM launch on the launch stream
-(`us_per_step_with_kernel_events`: the records add gaps between launches);
-those events give `gemm_kernels` and `roofline`, which describes the kernel
-that takes the most time per step.  `mfma_ceiling` is the MFMA-only rate on
-this workload's own codes (the part's clock depends on operand bit activity).  `cpu_baseline` times the
-CPU oracle on a bounded sample of the same step.  `mlp_chained` times the
-same step with the MLP chained as in a DiT block (the down layer's input is
-GELU, kept in BF16, of the up-projection's output): unfused (bf16 output,
-GELU kernel, quantizer) and fused (rudder_linear_gelu_quant).  `small_m` reports
-action/proprio-sized calls (96 and 192 rows against full-width weights) as
-achieved HBM GB/s, timed as graph replays.  `calibration` times the offline
-search of one layer's diagonal and layer-step table with the GPU in the loop.
+included); `us_per_step` is the mean latency of one step, timed over K steps
+with nothing but the step's launches on the stream, after W untimed steps
+(defaults: 20 timed steps after 5 warm-up steps, the latency protocol of the
+SteerQuant digest's efficiency appendix).  The same K steps then run twice
+more: once with an event at every step boundary (`step_us`: median, p10,
+p90), and once with an event triple around every linear on the launch stream
+(`us_per_step_with_kernel_events`: the records add gaps between launches).
+Those events give `per_call` (every linear's GEMM and quantize+GEMM time,
+median / p10 / p90), `gemm_kernels` and `roofline`, which describes the kernel
+that takes the most time per step.  `large_gemms` runs the hidden-4096
+backbone's linears (the largest W4A4 GEMMs) the same way.  `mfma_ceiling` is
+the MFMA-only rate on this workload's own codes (the part's clock depends on
+operand bit activity).  `cpu_baseline` times the CPU oracle on a bounded
+sample of the same step (1 warm-up + 3 timed runs, median).  `mlp_chained`
+times the same step with the MLP chained as in a DiT block (the down layer's
+input is GELU, kept in BF16, of the up-projection's output): unfused (bf16
+output, GELU kernel, quantizer) and fused (rudder_linear_gelu_quant).
+`small_m` reports action/proprio-sized calls (96 and 192 rows against
+full-width weights) as achieved HBM GB/s, timed as graph replays over
+rotating buffer sets that exceed the memory-side cache (and, for context, on
+one cache-resident set).  `calibration` times the offline search of one
+layer's diagonal and layer-step table with the GPU in the loop.
 
 --workload picks another workload (each printed as one JSON line of the
 same form, steps cycling through its step-indexed scale sets).
@@ -87,11 +93,12 @@ def kernel_source_hash() -> str:
 def parse_args():
     p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=32)
-    # ~40 ms of steps: the part's clocks reach their steady state under
-    # sustained load only after some tens of milliseconds (5 warmup steps:
-    # ~412 us per step, 100 or 300: ~370)
-    p.add_argument("--warmup", type=int, default=100)
+    # 20 timed steps after 5 warm-up steps, as in the pages' latency
+    # protocol.  The part's clocks settle under sustained load only after some
+    # tens of milliseconds; --warmup 100 gives the steady state of a long
+    # denoising loop.
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--w4a4-codes", choices=["int", "e2m3"], default="e2m3",
@@ -103,6 +110,8 @@ def parse_args():
                    help="skip the few-row (weight-streaming) calls")
     p.add_argument("--no-chained", action="store_true",
                    help="skip the chained-MLP (unfused / fused GELU + quantize) timing")
+    p.add_argument("--no-large", action="store_true",
+                   help="skip the per-call timing of the hidden-4096 backbone's linears")
     p.add_argument("--no-calibration", action="store_true",
                    help="skip the offline-calibration timing")
     p.add_argument("--no-ceiling", action="store_true",
@@ -111,8 +120,8 @@ def parse_args():
                    help="skip the library comparators (bf16 matmul, int8 GEMM)")
     p.add_argument("--cpu-rows", type=int, default=8384,
                    help="rows per linear in the CPU-oracle sample")
-    p.add_argument("--cpu-steps", type=int, default=6,
-                   help="denoising steps in the CPU-oracle sample")
+    p.add_argument("--cpu-step", type=int, default=0,
+                   help="denoising step whose scale set the CPU-oracle sample uses")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="before warmup, run a plain device copy of this many bytes three "
                         "times (a known-size reference for HBM byte counters)")
@@ -167,13 +176,16 @@ def prepare(wl_name: str, seed: int, torch, rudder, W, w4a4_codes: str = "int",
 
 
 def run_step(t: int, wl, sid_d, layers, rudder, ev=None):
-    """Enqueue one step (all linears).  ev: optional list of (start, end)
-    event pairs per layer, recorded around the GEMM launch."""
+    """Enqueue one step (all linears).  ev: optional list of (before quant_act,
+    before GEMM, after GEMM) event triples per layer, recorded on the launch
+    stream."""
     S, M = wl.S, wl.M
     T = wl.n_steps
     tt = t % T
     for i, Ly in enumerate(layers):
         K, N, abits, codes = Ly["K"], Ly["N"], Ly["abits"], Ly["codes"]
+        if ev is not None:
+            ev[i][0].record()
         if Ly["delta"] is None:
             rudder.rudder_quant_act(Ly["X"], sid_d, Ly["inv"], None, None, Ly["ws"], M, K, S,
                                     abits, codes, Ly["Xq"], Ly["rs"])
@@ -183,11 +195,11 @@ def run_step(t: int, wl, sid_d, layers, rudder, ev=None):
         ca = Ly["comp_a"][tt] if Ly["comp_a"].dim() == 3 else Ly["comp_a"]
         cb = Ly["comp_b"][tt] if Ly["comp_b"].dim() == 3 else Ly["comp_b"]
         if ev is not None:
-            ev[i][0].record()
+            ev[i][1].record()
         rudder.rudder_linear(Ly["Xq"], Ly["rs"], sid_d, Ly["Wq"], Ly["w_scale"], ca, cb, M, N, K,
                              S, abits, codes, Ly["Y"], None)
         if ev is not None:
-            ev[i][1].record()
+            ev[i][2].record()
 
 
 def run_chained_step(t: int, wl, sid_d, layers, rudder, fused: bool, gelu_buf):
@@ -292,6 +304,23 @@ def mfma_ceiling(layers, rudder, torch, iters: int = 4000, reps: int = 5):
             e1.record()
             torch.cuda.synchronize()
             res[name] = round(ops * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        if codes != rudder.CODES_E2M3:
+            # the other int8 instruction shape on the same codes
+            shape = rudder.CEILING_I8_16X16X64
+            run = lambda: rudder.rudder_mfma_ceiling_shape(Ly["Xq"], Ly["Wq"], M, N, K, abits,
+                                                           codes, iters, shape, sink)
+            for _ in range(3):
+                run()
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            res["workload_codes_tops_i8_16x16x64"] = round(
+                ops * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
         res["layer"] = f"{Ly['name']} {K}->{N}"
         out[tag] = res
     return out
@@ -311,10 +340,20 @@ def load_traffic(kernel_tag: str, src_hash: str):
     return ent.get("bytes_per_launch")
 
 
-def cpu_baseline(wi, rows_per_layer: int, n_steps: int, seed: int):
-    """Time the CPU oracle (quantize -> integer GEMM -> epilogue) on a
-    bounded sample of the workload: rows_per_layer rows through every linear
-    for the first n_steps step-indexed scale sets."""
+def cpu_baseline(wi, rows_per_layer: int, step: int, seed: int):
+    """Time the CPU oracle (quantize -> integer GEMM -> epilogue) on a bounded
+    sample of the workload: rows_per_layer rows through every linear at one
+    step's scale set, 1 untimed warm-up run then 3 timed runs, median.  The
+    OpenMP thread count is the process's CPU affinity count (capped by an
+    OMP_NUM_THREADS already set in the environment), set before the oracle
+    library starts OpenMP."""
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS")
+    threads = min(affinity, int(env)) if env and env.isdigit() and int(env) > 0 else affinity
+    os.environ["OMP_NUM_THREADS"] = str(threads)
     import oracle
     wl = wi.workload
     rng = np.random.default_rng(seed)
@@ -327,10 +366,10 @@ def cpu_baseline(wi, rows_per_layer: int, n_steps: int, seed: int):
         qw, ws = oracle.quantize_weights(L.w, L.smooth)          # offline, untimed
         x = np.ascontiguousarray(L.x[rows])
         prepared.append((L, inv, qw, ws, x))
-    steps = max(1, min(n_steps, wl.n_steps))
-    ops = 0
-    t0 = time.perf_counter()
-    for t in range(steps):
+    t = step % wl.n_steps
+
+    def one_run():
+        ops = 0
         for (L, inv, qw, ws, x) in prepared:
             if L.act_scale is None:
                 delta = oracle.dynamic_scales(x, sid, inv, wl.S, L.layer.abits)
@@ -339,11 +378,20 @@ def cpu_baseline(wi, rows_per_layer: int, n_steps: int, seed: int):
             a, b = L.step_comp(t)
             oracle.linear(x, sid, qw, ws, inv, delta, a, b, wl.S, L.layer.abits)
             ops += 2 * len(rows) * L.layer.K * L.layer.N
-    dt = time.perf_counter() - t0
+        return ops
+
+    one_run()                                                   # warm-up
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        ops = one_run()
+        times.append(time.perf_counter() - t0)
+    dt = float(np.median(times))
     return dict(value=ops / dt / 1e12, unit="TOPS", cores=oracle.num_threads(), kind="oracle",
-                sample=f"{len(rows)} of {M} rows through all {len(wi.layers)} linears for "
-                       f"steps 0..{steps - 1} (quantize + int32 GEMM + epilogue), "
-                       f"{dt:.1f} s wall")
+                sample=f"{len(rows)} of {M} rows through all {len(wi.layers)} linears at step "
+                       f"{t} (quantize + int32 GEMM + epilogue); 1 warm-up + 3 timed runs, "
+                       f"median {dt:.2f} s per run",
+                affinity_cpus=affinity, runs_s=[round(x, 3) for x in times])
 
 
 def bf16_comparator(wl, layers, torch, reps: int = 10):
@@ -402,11 +450,20 @@ SMALL_M_CASES = (
 )
 
 
-def small_m_calls(torch, rudder, w4a4_codes: str, reps: int = 20):
-    """Few-row calls timed as graph replays of `reps` back-to-back calls (a
-    few-µs kernel is otherwise timed by the host's issue rate).  Reports the
-    GEMM kernel alone and quant_act + linear, with the GEMM's algorithmic
-    bytes (packed weights + codes in + bf16 out + scales) per second."""
+MALL_BYTES = 256 * 2**20          # MI355X memory-side (Infinity) cache
+
+
+def small_m_calls(torch, rudder, w4a4_codes: str, warm_reps: int = 20):
+    """Few-row calls, each timed two ways as graph replays (a few-µs kernel
+    is otherwise timed by the host's issue rate):
+      - cold: one call per buffer set, cycling through at least 8 distinct
+        sets (packed weights, codes, scales, outputs) that together hold more
+        than 3x the memory-side cache, so every call reads its operands from
+        HBM;
+      - warm: `warm_reps` calls on the same set (operands cache-resident).
+    Reports the GEMM kernel alone and quant_act + linear, with the GEMM's
+    algorithmic bytes (packed weights + codes in + bf16 out + scales) per
+    second."""
     out = {}
     S = 3
     gen = torch.Generator(device="cuda")
@@ -414,35 +471,45 @@ def small_m_calls(torch, rudder, w4a4_codes: str, reps: int = 20):
     for name, M, K, N, abits, codes_name in SMALL_M_CASES:
         codes = rudder.CODES_E2M3 if (abits == 4 and (codes_name == "e2m3" and
                                                       w4a4_codes == "e2m3")) else rudder.CODES_INT
-        X = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
-        Wt = (torch.randn(K, N, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
-        smooth = torch.ones(K, device="cuda")
+        wbytes = 0.75 if codes == rudder.CODES_E2M3 else 0.5
+        abytes = 0.75 if codes == rudder.CODES_E2M3 else abits / 8
+        gemm_bytes = N * K * wbytes + M * K * abytes + 2 * M * N + 4 * N + 8 * S * N + 5 * M
+        set_bytes = gemm_bytes + 2 * M * K                       # + the bf16 input X
+        n_sets = max(8, int(np.ceil(3 * MALL_BYTES / set_bytes)))
         sid = (torch.arange(M, device="cuda") % S).to(torch.uint8)
-        Wq, ws, inv = rudder.quantize_weights(Wt, smooth, codes)
+        smooth = torch.ones(K, device="cuda")
         delta = torch.tensor([0.02, 0.03, 0.025], device="cuda")
-        ca = torch.rand(S, N, device="cuda", generator=gen) + 0.5
-        cb = torch.randn(S, N, device="cuda", generator=gen) * 0.01
-        Xq, rs = rudder.quant_act(X, sid, inv, delta, S, abits, codes)
-        Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+        sets = []
+        for _ in range(n_sets):
+            X = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+            Wt = (torch.randn(K, N, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+            Wq, ws, inv = rudder.quantize_weights(Wt, smooth, codes)
+            del Wt
+            ca = torch.rand(S, N, device="cuda", generator=gen) + 0.5
+            cb = torch.randn(S, N, device="cuda", generator=gen) * 0.01
+            Xq, rs = rudder.quant_act(X, sid, inv, delta, S, abits, codes)
+            Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+            sets.append((X, Wq, ws, inv, ca, cb, Xq, rs, Y))
 
-        def gemm():
+        def gemm(i):
+            X, Wq, ws, inv, ca, cb, Xq, rs, Y = sets[i]
             rudder.rudder_linear(Xq, rs, sid, Wq, ws, ca, cb, M, N, K, S, abits, codes, Y)
 
-        def pair():
+        def pair(i):
+            X, Wq, ws, inv, ca, cb, Xq, rs, Y = sets[i]
             rudder.rudder_quant_act(X, sid, inv, delta, None, None, M, K, S, abits, codes, Xq, rs)
-            gemm()
+            gemm(i)
 
-        res = {}
-        for label, fn in (("gemm", gemm), ("quant_act+gemm", pair)):
-            for _ in range(3):
-                fn()
+        def replay_us(seq, fn):
+            for i in seq[:3]:
+                fn(i)
             torch.cuda.synchronize()
             g = torch.cuda.CUDAGraph()
             st = torch.cuda.Stream()
             with torch.cuda.stream(st):
                 with torch.cuda.graph(g, stream=st):
-                    for _ in range(reps):
-                        fn()
+                    for i in seq:
+                        fn(i)
             torch.cuda.synchronize()
             g.replay()
             best = 1e9
@@ -454,19 +521,29 @@ def small_m_calls(torch, rudder, w4a4_codes: str, reps: int = 20):
                 g.replay()
                 e1.record()
                 torch.cuda.synchronize()
-                best = min(best, e0.elapsed_time(e1) / reps)
-            res[label] = best * 1e3
-        wbytes = 0.75 if codes == rudder.CODES_E2M3 else 0.5
-        abytes = 0.75 if codes == rudder.CODES_E2M3 else abits / 8
-        gemm_bytes = N * K * wbytes + M * K * abytes + 2 * M * N + 4 * N + 8 * S * N + 5 * M
-        gbs = gemm_bytes / (res["gemm"] * 1e-6) / 1e9
+                best = min(best, e0.elapsed_time(e1) / len(seq))
+            del g
+            return best * 1e3
+
+        cold = list(range(n_sets))
+        warm = [0] * warm_reps
+        res = {"gemm_cold": replay_us(cold, gemm), "pair_cold": replay_us(cold, pair),
+               "gemm_warm": replay_us(warm, gemm), "pair_warm": replay_us(warm, pair)}
+        gbs = gemm_bytes / (res["gemm_cold"] * 1e-6) / 1e9
+        gbs_w = gemm_bytes / (res["gemm_warm"] * 1e-6) / 1e9
         out[name] = {"M": M, "K": K, "N": N,
                      "codes": "e2m3" if codes == rudder.CODES_E2M3 else "int",
-                     "gemm_us": round(res["gemm"], 2),
-                     "quant_act_plus_gemm_us": round(res["quant_act+gemm"], 2),
+                     "gemm_us": round(res["gemm_cold"], 2),
+                     "quant_act_plus_gemm_us": round(res["pair_cold"], 2),
                      "gemm_bytes": int(gemm_bytes), "gemm_GBps": round(gbs, 1),
-                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
-        del X, Wt, Wq, Xq, Y
+                     "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                     "buffer_sets": n_sets,
+                     "buffer_set_MB": round(set_bytes / 1e6, 1),
+                     "mall_warm": {"gemm_us": round(res["gemm_warm"], 2),
+                                   "quant_act_plus_gemm_us": round(res["pair_warm"], 2),
+                                   "gemm_GBps": round(gbs_w, 1)}}
+        del sets
+        torch.cuda.empty_cache()
     return out
 
 
@@ -488,6 +565,110 @@ def calibration_run(torch, W):
     return {"layer": "qkv 2048->6144 W4A8", "rows_per_step": 256, "steps": 4,
             "passes": res.passes, "ms": round(dt * 1e3, 1),
             "alpha": res.alpha, "rho_index": res.rho_index}
+
+
+def _events(n):
+    import torch
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
+
+def _dist(xs_us):
+    """median / p10 / p90 of a list of microsecond values."""
+    a = np.asarray(xs_us, np.float64)
+    return {"median": round(float(np.median(a)), 2), "p10": round(float(np.percentile(a, 10)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2)}
+
+
+def instrumented_steps(wl, sid_d, layers, rudder, torch, steps: int, t0: int = 0):
+    """`steps` steps with an event triple around every linear (quant_act, GEMM)
+    on the launch stream.  Returns per-layer lists of (quant+GEMM µs, GEMM µs)
+    and the step time of this pass (the records add small gaps)."""
+    ev = [[_events(3) for _ in layers] for _ in range(steps)]
+    start, end = _events(2)
+    torch.cuda.synchronize()
+    start.record()
+    for t in range(steps):
+        run_step(t0 + t, wl, sid_d, layers, rudder, ev[t])
+    end.record()
+    torch.cuda.synchronize()
+    per = [([], []) for _ in layers]
+    for t in range(steps):
+        for i in range(len(layers)):
+            e = ev[t][i]
+            per[i][0].append(e[0].elapsed_time(e[2]) * 1e3)
+            per[i][1].append(e[1].elapsed_time(e[2]) * 1e3)
+    return per, start.elapsed_time(end) / steps * 1e3
+
+
+def per_call_table(wl, layers, per, rudder, tag_prefix=""):
+    """Per-linear call statistics (median / p10 / p90 over the timed steps) of
+    rudder_linear alone and of rudder_quant_act + rudder_linear, with the
+    GEMM's rate against the int8 and FP6 matrix-core peaks."""
+    out = {}
+    for Ly, (pair, gemm) in zip(layers, per):
+        ops = 2.0 * wl.M * Ly["N"] * Ly["K"]
+        med = float(np.median(gemm))
+        tops = ops / (med * 1e-6) / 1e12
+        e2m3 = Ly["codes"] == rudder.CODES_E2M3
+        key = (f"{tag_prefix}{Ly['name']} {wl.M}x{Ly['K']}->{Ly['N']} W4A{Ly['abits']}"
+               f"{' e2m3' if e2m3 else ''}")
+        ent = {"gemm_us": _dist(gemm), "quant_act_plus_gemm_us": _dist(pair),
+               "gemm_tops": round(tops, 1),
+               "fused_linear_tops": round(ops / (float(np.median(pair)) * 1e-6) / 1e12, 1),
+               "pct_int8_peak": round(100 * tops / INT8_PEAK_TOPS, 1)}
+        if e2m3:
+            peak = FP6_PEAK_TFLOPS / (2 if Ly["abits"] == 8 else 1)
+            ent["pct_fp6_peak"] = round(100 * tops / peak, 1)
+        out[key] = ent
+    return out
+
+
+def large_gemm_calls(args, torch, rudder, W, steps: int = 20, warmup: int = 5):
+    """The hidden-4096 backbone's four linears (16576 rows; QKV, O, MLP up and
+    down, all W4A4), drawn with the workload generator and run as that
+    workload's step loop (each layer's weights were last read a whole step
+    earlier, as in a model): `warmup` untimed steps, then `steps` steps with
+    per-call events."""
+    name = "backbone_h4096_m16576_w4a4"
+    wi, sid_d, layers = prepare(name, args.seed, torch, rudder, W, args.w4a4_codes,
+                                args.w4a8_codes)
+    wl = wi.workload
+    for t in range(warmup):
+        run_step(t, wl, sid_d, layers, rudder)
+    per, step_us = instrumented_steps(wl, sid_d, layers, rudder, torch, steps, warmup)
+    res = per_call_table(wl, layers, per, rudder)
+    res["step_us_with_events"] = round(step_us, 1)
+    res["protocol"] = f"{warmup} warm-up steps, {steps} timed steps, HIP events per call"
+    del layers, sid_d, wi
+    torch.cuda.empty_cache()
+    return res
+
+
+# The measured limiter of each GEMM kernel's main loop (from timing-only
+# variants and counters; the roofline bound stays the matrix cores, whose
+# arithmetic intensity is far above the HBM ridge).
+LIMITER = {
+    "w4a4_e2m3_gemm": "operand stream from L2 to the compute units (latency-bound loads)",
+    "w4a8_e2m3_gemm": "operand stream from L2 to the compute units (latency-bound loads)",
+    "w4a8_gemm": "matrix-core rate at the operands' power-limited clock",
+    "w4a4_gemm": "matrix-core rate at the operands' power-limited clock",
+}
+
+
+def path_dtype(layers, rudder) -> str:
+    """The arithmetic types the step's contractions run in: int8 MFMA with
+    int32 sums (int containers), FP6 E2M3 MFMA with fp32 sums that hold exact
+    integers (4-bit E2M3 codes), two FP6 MFMAs per product (8-bit codes as
+    E2M3 digit planes)."""
+    kinds = []
+    for Ly in layers:
+        if Ly["codes"] != rudder.CODES_E2M3:
+            k = "int8"
+        else:
+            k = "fp6_e2m3" if Ly["abits"] == 4 else "fp6_e2m3_x2"
+        if k not in kinds:
+            kinds.append(k)
+    return "+".join(kinds)
 
 
 def main():
@@ -536,31 +717,31 @@ def main():
     total_ms = start.elapsed_time(end)
     ms_per_step = total_ms / args.steps
 
-    # The same K steps again with a HIP event pair around every GEMM launch
-    # (on the launch stream), for the per-kernel durations.  The event
-    # records add gaps between launches, so this pass is kept out of the
-    # headline; its step time is reported beside it.
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in layers] for _ in range(args.steps)]
-    start_i = torch.cuda.Event(enable_timing=True)
-    end_i = torch.cuda.Event(enable_timing=True)
+    # Per-step distribution: the same K steps again with one event at every
+    # step boundary (median / p10 / p90 of the step time).
+    bounds = _events(args.steps + 1)
     torch.cuda.synchronize()
-    start_i.record()
+    bounds[0].record()
     for t in range(args.steps):
-        run_step(t, wl, sid_d, layers, rudder, ev[t])
-    end_i.record()
+        run_step(t, wl, sid_d, layers, rudder)
+        bounds[t + 1].record()
     torch.cuda.synchronize()
-    ms_per_step_instrumented = start_i.elapsed_time(end_i) / args.steps
+    step_dist = _dist([bounds[t].elapsed_time(bounds[t + 1]) * 1e3 for t in range(args.steps)])
+
+    # The same K steps again with an event triple around every linear (on the
+    # launch stream), for the per-kernel durations.  The event records add
+    # gaps between launches, so this pass is kept out of the headline; its
+    # step time is reported beside it.
+    per, us_instrumented = instrumented_steps(wl, sid_d, layers, rudder, torch, args.steps)
+    ms_per_step_instrumented = us_instrumented * 1e-3
 
     # per-kernel (GEMM) launch durations, grouped by kernel instance (abits)
     gemm_ms = {}
     gemm_ops = {}
-    for t in range(args.steps):
-        for i, Ly in enumerate(layers):
-            d = ev[t][i][0].elapsed_time(ev[t][i][1])
-            key = gemm_kernel_tag(Ly, rudder)
-            gemm_ms.setdefault(key, []).append(d)
-            gemm_ops.setdefault(key, []).append(2 * wl.M * Ly["N"] * Ly["K"])
+    for i, Ly in enumerate(layers):
+        key = gemm_kernel_tag(Ly, rudder)
+        gemm_ms.setdefault(key, []).extend(d * 1e-3 for d in per[i][1])
+        gemm_ops.setdefault(key, []).extend([2 * wl.M * Ly["N"] * Ly["K"]] * args.steps)
     dominant = max(gemm_ms, key=lambda k: sum(gemm_ms[k]))
     avg_ms = float(np.mean(gemm_ms[dominant]))
     ops_per_launch = float(np.mean(gemm_ops[dominant]))
@@ -592,13 +773,14 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
         "us_per_step": round(ms_per_step * 1e3, 1),
+        "step_us": step_dist,
         "us_per_step_with_kernel_events": round(ms_per_step_instrumented * 1e3, 1),
         "pct_int8_peak": round(100 * value / INT8_PEAK_TOPS, 2),
         "gemm_only_tops": round(ops_step / (gemm_only_ms * 1e-3) / 1e12, 2),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "int8",
+        "dtype": path_dtype(layers, rudder),
         "data": "synthetic",
         "config": {
             "workload": wl.name,
@@ -613,6 +795,7 @@ def main():
         "roofline": {
             "kernel": dominant,
             "bound": "mfma",
+            "limiter": LIMITER.get(dominant),
             "achieved": round(achieved, 2),
             "peak": dom_peak,
             "unit": "TFLOP/s",
@@ -624,6 +807,7 @@ def main():
             "source_hash": src_hash,
         },
         "gemm_kernels": per_kernel,
+        "per_call": per_call_table(wl, layers, per, rudder),
         "wall_s": round(wall, 3),
     }
     if not args.no_ceiling:
@@ -647,10 +831,12 @@ def main():
         out["mlp_chained"] = chained
     if not args.no_small_m:
         out["small_m"] = small_m_calls(torch, rudder, args.w4a4_codes)
+    if not args.no_large and args.workload != "backbone_h4096_m16576_w4a4":
+        out["large_gemms"] = large_gemm_calls(args, torch, rudder, W)
     if not args.no_calibration:
         out["calibration"] = calibration_run(torch, W)
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.cpu_steps, args.seed)
+        out["cpu_baseline"] = cpu_baseline(wi, args.cpu_rows, args.cpu_step, args.seed)
     print(json.dumps(out), flush=True)
 
 

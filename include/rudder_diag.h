@@ -58,6 +58,22 @@ double rudder_mfma_ceiling_ops(int iters, int codes);
 rudder_status_t rudder_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K,
                                     int abits, int codes, int iters, int32_t* sink, void* stream);
 
+/* Instruction shapes for rudder_mfma_ceiling_shape. */
+#define RUDDER_CEILING_OWN 0           /* the instruction rudder_linear uses */
+#define RUDDER_CEILING_I8_16X16X64 1   /* v_mfma_i32_16x16x64_i8 (int containers) */
+
+/* rudder_mfma_ceiling with a choice of matrix-core instruction: `shape`
+ * RUDDER_CEILING_OWN is rudder_mfma_ceiling itself; RUDDER_CEILING_I8_16X16X64
+ * feeds the same int8 fragments (int4 codes widened) to
+ * v_mfma_i32_16x16x64_i8, two instructions per 32x32x32 product of the
+ * pattern, so that rudder_mfma_ceiling_ops(iters, RUDDER_CODES_INT) still
+ * counts the ops of a launch.  Errors as for rudder_mfma_ceiling, plus
+ * RUDDER_ERR_INVALID_ARG for an unknown shape or RUDDER_CEILING_I8_16X16X64
+ * with codes other than RUDDER_CODES_INT. */
+rudder_status_t rudder_mfma_ceiling_shape(const uint8_t* Xq, const uint8_t* Wq, int M, int N,
+                                          int K, int abits, int codes, int iters, int shape,
+                                          int32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,7 +64,11 @@ constexpr int kDigitScaleWord = 127 | (127 + 5) << 8 | (127 + 1) << 16;
 // ABITS 8: int8 activations x int4 weights (int8 MFMA); ABITS 4 with
 // E2M3 = false: int4 x int4 widened to int8; E2M3: FP6 f8f6f4 MFMA (ABITS
 // 8: two MFMAs per product, one per digit plane of the activation codes).
-template <int ABITS, bool E2M3>
+// SHAPE16 (int containers only): the same fragments fed to
+// v_mfma_i32_16x16x64_i8 instead, two instructions (half the ops each) per
+// 32x32x32 product of the pattern, into 16 independent accumulators, so an
+// iteration carries the same op count.
+template <int ABITS, bool E2M3, bool SHAPE16 = false>
 __global__ __launch_bounds__(kThreads, 2) void mfma_ceiling_kernel(
     const uint8_t* __restrict__ Xq, uint32_t act_blocks, const uint8_t* __restrict__ Wq,
     uint32_t w_blocks, int iters, int32_t* __restrict__ sink) {
@@ -168,21 +172,42 @@ __global__ __launch_bounds__(kThreads, 2) void mfma_ceiling_kernel(
                 }
             }
         }
-        v16i acc[kFW][kFA] = {};
-        for (int it = 0; it < iters; ++it) {
+        if constexpr (SHAPE16) {
+            v4i acc[kFW][kFA][2] = {};
+            for (int it = 0; it < iters; ++it) {
 #pragma unroll
-            for (int s = 0; s < kSets; ++s)
+                for (int s = 0; s < kSets; ++s)
 #pragma unroll
-                for (int f = 0; f < kFW; ++f)
+                    for (int f = 0; f < kFW; ++f)
 #pragma unroll
-                    for (int g = 0; g < kFA; ++g)
-                        acc[f][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(wf[s][f], af[s][g],
-                                                                      acc[f][g], 0, 0, 0);
+                        for (int g = 0; g < kFA; ++g) {
+                            acc[f][g][0] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                wf[s][f], af[s][g], acc[f][g][0], 0, 0, 0);
+                            acc[f][g][1] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                                af[s][g], wf[s][f], acc[f][g][1], 0, 0, 0);
+                        }
+            }
+#pragma unroll
+            for (int f = 0; f < kFW; ++f)
+#pragma unroll
+                for (int g = 0; g < kFA; ++g) out += acc[f][g][0][lane & 3] + acc[f][g][1][lane & 3];
+        } else {
+            v16i acc[kFW][kFA] = {};
+            for (int it = 0; it < iters; ++it) {
+#pragma unroll
+                for (int s = 0; s < kSets; ++s)
+#pragma unroll
+                    for (int f = 0; f < kFW; ++f)
+#pragma unroll
+                        for (int g = 0; g < kFA; ++g)
+                            acc[f][g] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                                wf[s][f], af[s][g], acc[f][g], 0, 0, 0);
+            }
+#pragma unroll
+            for (int f = 0; f < kFW; ++f)
+#pragma unroll
+                for (int g = 0; g < kFA; ++g) out += acc[f][g][lane & 15];
         }
-#pragma unroll
-        for (int f = 0; f < kFW; ++f)
-#pragma unroll
-            for (int g = 0; g < kFA; ++g) out += acc[f][g][lane & 15];
     }
     sink[blockIdx.x * kThreads + threadIdx.x] = out;
 }
@@ -201,12 +226,21 @@ double mfma_ceiling_ops(int iters, int codes) {
 
 hipError_t launch_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K,
                                int abits, int codes, int iters, int32_t* sink,
-                               hipStream_t stream) {
+                               hipStream_t stream, int shape) {
     const int ksub = codes == RUDDER_CODES_E2M3 ? 64 : 32;
     const uint32_t kb = (uint32_t)(K / ksub);
     const uint32_t act_blocks = (uint32_t)((M + 31) / 32) * kb;
     const uint32_t w_blocks = (uint32_t)(N / 32) * kb;
     const dim3 grid(RUDDER_CEILING_BLOCKS), block(kThreads);
+    if (shape == RUDDER_CEILING_I8_16X16X64) {
+        if (abits == 8)
+            hipLaunchKernelGGL((mfma_ceiling_kernel<8, false, true>), grid, block, 0, stream, Xq,
+                               act_blocks, Wq, w_blocks, iters, sink);
+        else
+            hipLaunchKernelGGL((mfma_ceiling_kernel<4, false, true>), grid, block, 0, stream, Xq,
+                               act_blocks, Wq, w_blocks, iters, sink);
+        return hipGetLastError();
+    }
     if (codes == RUDDER_CODES_E2M3 && abits == 8)
         hipLaunchKernelGGL((mfma_ceiling_kernel<8, true>), grid, block, 0, stream, Xq, act_blocks,
                            Wq, w_blocks, iters, sink);

@@ -270,7 +270,18 @@ double rudder_mfma_ceiling_ops(int iters, int codes) {
 rudder_status_t rudder_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K,
                                     int abits, int codes, int iters, int32_t* sink,
                                     void* stream) {
+    return rudder_mfma_ceiling_shape(Xq, Wq, M, N, K, abits, codes, iters, RUDDER_CEILING_OWN,
+                                     sink, stream);
+}
+
+rudder_status_t rudder_mfma_ceiling_shape(const uint8_t* Xq, const uint8_t* Wq, int M, int N,
+                                          int K, int abits, int codes, int iters, int shape,
+                                          int32_t* sink, void* stream) {
     const char* f = "rudder_mfma_ceiling";
+    if (shape != RUDDER_CEILING_OWN && shape != RUDDER_CEILING_I8_16X16X64)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown instruction shape %d", f, shape);
+    if (shape == RUDDER_CEILING_I8_16X16X64 && codes != RUDDER_CODES_INT)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: the 16x16x64 int8 shape takes int codes", f);
     if (!Xq || !Wq || !sink) return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
     if (misaligned(Xq) || misaligned(Wq) || misaligned(sink))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: Xq, Wq and sink must be 16-byte aligned", f);
@@ -286,7 +297,7 @@ rudder_status_t rudder_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M,
     if (iters <= 0 || iters > (1 << 24))
         return fail(RUDDER_ERR_INVALID_ARG, "%s: iters=%d must be in 1..2^24", f, iters);
     return from_hip(rudder::launch_mfma_ceiling(Xq, Wq, M, N, K, abits, codes, iters, sink,
-                                                static_cast<hipStream_t>(stream)),
+                                                static_cast<hipStream_t>(stream), shape),
                     f);
 }
 

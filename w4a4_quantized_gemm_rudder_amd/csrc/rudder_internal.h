@@ -62,7 +62,7 @@ size_t mfma_ceiling_sink_bytes();
 double mfma_ceiling_ops(int iters, int codes);
 hipError_t launch_mfma_ceiling(const uint8_t* Xq, const uint8_t* Wq, int M, int N, int K,
                                int abits, int codes, int iters, int32_t* sink,
-                               hipStream_t stream);
+                               hipStream_t stream, int shape = RUDDER_CEILING_OWN);
 
 // ---------------------------------------------------------------------------
 // Device helpers

@@ -40,6 +40,7 @@ EXPORTED = (
     "rudder_dequant_weights", "rudder_stream_sq_error_workspace_bytes", "rudder_stream_sq_error",
     "rudder_status_string", "rudder_last_error",
     "rudder_mfma_ceiling_sink_bytes", "rudder_mfma_ceiling_ops", "rudder_mfma_ceiling",
+    "rudder_mfma_ceiling_shape",
 )
 
 _lib: Optional[ctypes.CDLL] = None
@@ -91,6 +92,8 @@ def load_library() -> ctypes.CDLL:
     lib.rudder_mfma_ceiling_ops.restype = ctypes.c_double
     lib.rudder_mfma_ceiling.argtypes = [vp, vp, i, i, i, i, i, i, vp, vp]
     lib.rudder_mfma_ceiling.restype = i
+    lib.rudder_mfma_ceiling_shape.argtypes = [vp, vp, i, i, i, i, i, i, i, vp, vp]
+    lib.rudder_mfma_ceiling_shape.restype = i
     lib.rudder_status_string.argtypes = [i]
     lib.rudder_status_string.restype = ctypes.c_char_p
     lib.rudder_last_error.argtypes = []
@@ -286,3 +289,13 @@ def rudder_mfma_ceiling(Xq, Wq, M: int, N: int, K: int, abits: int, codes: int, 
                         sink, stream=None) -> None:
     _check(load_library().rudder_mfma_ceiling(_ptr(Xq), _ptr(Wq), M, N, K, abits, codes, iters,
                                               _ptr(sink), _stream(stream)))
+
+
+CEILING_OWN = 0             # the instruction rudder_linear uses
+CEILING_I8_16X16X64 = 1     # v_mfma_i32_16x16x64_i8 (int containers)
+
+
+def rudder_mfma_ceiling_shape(Xq, Wq, M: int, N: int, K: int, abits: int, codes: int,
+                              iters: int, shape: int, sink, stream=None) -> None:
+    _check(load_library().rudder_mfma_ceiling_shape(_ptr(Xq), _ptr(Wq), M, N, K, abits, codes,
+                                                    iters, shape, _ptr(sink), _stream(stream)))

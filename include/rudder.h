@@ -33,8 +33,9 @@
  *   - Every buffer pointer is a DEVICE pointer (hipMalloc'd or torch CUDA
  *     memory) unless stated otherwise; `stream` is a hipStream_t passed as
  *     void* (NULL = the default stream).
- *   - The caller owns and allocates every buffer; the library keeps no device
- *     state and never allocates.
+ *   - The caller owns and allocates every buffer; the library never
+ *     allocates, and its only device state is the fixed scratch array of
+ *     rudder_quant_act_noalloc (one per GPU, from that call's first use).
  *   - Calls are asynchronous: they return once the work is enqueued on
  *     `stream`; results are valid after the stream is synchronized.  Calls
  *     are thread-safe.
@@ -195,6 +196,31 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
                                  float* act_scale_out, void* workspace,
                                  int M, int K, int S, int abits, int codes,
                                  void* Xq, float* row_scale, void* stream);
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, serving loops, harnesses that forbid hipMalloc): the dynamic mode
+ * of rudder_quant_act (act_scale = NULL) without a workspace argument.  The
+ * partial maxima and step sizes live in a scratch array the library holds
+ * per GPU, RUDDER_MAX_STREAMS * 1025 floats (32,800 bytes), from the first
+ * call on that GPU until the process ends; the call itself allocates
+ * nothing.  The scratch size does not depend on M or K, so every size
+ * rudder_quant_act accepts fits.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (several streams or threads) race
+ * and must be serialized by the caller.  The device current on the calling
+ * thread must be the device of `stream`.
+ *
+ *   arguments as for rudder_quant_act in dynamic mode; act_scale_out may be
+ *   NULL
+ * Results are identical to rudder_quant_act(X, stream_id, inv_smooth, NULL,
+ * act_scale_out, workspace, ...).
+ * Errors: those of rudder_quant_act (dynamic mode); RUDDER_ERR_HIP also when
+ * the scratch's device address cannot be obtained.
+ */
+rudder_status_t rudder_quant_act_noalloc(const uint16_t* X, const uint8_t* stream_id,
+                                         const float* inv_smooth, float* act_scale_out,
+                                         int M, int K, int S, int abits, int codes,
+                                         void* Xq, float* row_scale, void* stream);
 
 /*
  * Low-bit GEMM with fused epilogue (SteerQuant §4.4: low-bit GEMM followed by

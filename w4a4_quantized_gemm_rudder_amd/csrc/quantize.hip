@@ -11,6 +11,8 @@
 //
 // Both kernels are HBM-streaming codecs: no MFMA work, coalesced 16-byte
 // loads of bf16 and contiguous stores of the MFMA-tiled code layout.
+#include <mutex>
+
 #include "rudder_internal.h"
 
 namespace rudder {
@@ -439,6 +441,63 @@ hipError_t launch_quant_act_dynamic(const uint16_t* X, const uint8_t* sid,
     if (e != hipSuccess) return e;
     return launch_quant_act_static(X, sid, inv_smooth, delta, M, K, S, abits, codes, Xq,
                                    row_scale, stream);
+}
+
+}  // namespace rudder
+
+// ---------------------------------------------------------------------------
+// Scratch of the no-allocation dynamic-mode entry point: the partial maxima
+// and step sizes that rudder_quant_act keeps in its caller's workspace
+// (RUDDER_MAX_STREAMS * (kMaxPartials + 1) floats, the same layout).  Each
+// GPU holds its own copy until the process ends; every call on a GPU shares
+// it, so calls that overlap on one GPU race.  Nothing in it has to start at
+// zero: each call writes every partial it reads.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[RUDDER_MAX_STREAMS * (1024 + 1)];
+
+namespace rudder {
+namespace {
+
+static_assert(sizeof(scratch) == sizeof(float) * RUDDER_MAX_STREAMS * (kMaxPartials + 1),
+              "scratch holds the dynamic-mode workspace");
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept.  In host code the array's
+// name is only a host-side stand-in, so kernels get this address instead.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+size_t quant_act_noalloc_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t launch_quant_act_dynamic_noalloc(const uint16_t* X, const uint8_t* sid,
+                                            const float* inv_smooth, float* act_scale_out,
+                                            int M, int K, int S, int abits, int codes, void* Xq,
+                                            float* row_scale, hipStream_t stream) {
+    void* ws = nullptr;
+    const hipError_t e = scratch_address(&ws);
+    if (e != hipSuccess) return e;
+    return launch_quant_act_dynamic(X, sid, inv_smooth, act_scale_out, ws, M, K, S, abits, codes,
+                                    Xq, row_scale, stream);
 }
 
 }  // namespace rudder

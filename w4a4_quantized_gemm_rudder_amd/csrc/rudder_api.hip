@@ -126,6 +126,43 @@ rudder_status_t rudder_quant_act(const uint16_t* X, const uint8_t* stream_id,
                     f);
 }
 
+rudder_status_t rudder_quant_act_noalloc(const uint16_t* X, const uint8_t* stream_id,
+                                         const float* inv_smooth, float* act_scale_out, int M,
+                                         int K, int S, int abits, int codes, void* Xq,
+                                         float* row_scale, void* stream) {
+    const char* f = "rudder_quant_act_noalloc";
+    if (!X || !stream_id || !inv_smooth || !Xq || !row_scale)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: null pointer argument", f);
+    if (M < 0 || K <= 0)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: M=%d must be >= 0 and K=%d > 0", f, M, K);
+    if (K % 32) return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 32", f, K);
+    if (S < 1 || S > RUDDER_MAX_STREAMS)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: S=%d must be in 1..%d", f, S, RUDDER_MAX_STREAMS);
+    if (abits != 4 && abits != 8)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: abits=%d must be 4 or 8", f, abits);
+    if (codes != RUDDER_CODES_INT && codes != RUDDER_CODES_E2M3)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: unknown code container %d", f, codes);
+    if (codes == RUDDER_CODES_E2M3 && K % 64)
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: K=%d must be a multiple of 64 for E2M3 codes",
+                    f, K);
+    if (misaligned(X) || misaligned(inv_smooth) || misaligned(Xq))
+        return fail(RUDDER_ERR_INVALID_ARG, "%s: X, inv_smooth and Xq must be 16-byte aligned",
+                    f);
+    if (K > RUDDER_MAX_K)
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: K=%d exceeds %d", f, K, RUDDER_MAX_K);
+    // the scratch holds the fixed-size dynamic-mode workspace, whatever M and K
+    if (rudder::quant_act_workspace_bytes() > rudder::quant_act_noalloc_scratch_bytes())
+        return fail(RUDDER_ERR_UNSUPPORTED, "%s: the workspace (%zu bytes) exceeds the scratch "
+                    "(%zu bytes)", f, rudder::quant_act_workspace_bytes(),
+                    rudder::quant_act_noalloc_scratch_bytes());
+    if (M == 0) return ok();
+    return from_hip(rudder::launch_quant_act_dynamic_noalloc(X, stream_id, inv_smooth,
+                                                             act_scale_out, M, K, S, abits, codes,
+                                                             Xq, row_scale,
+                                                             static_cast<hipStream_t>(stream)),
+                    f);
+}
+
 namespace {
 
 // Checks shared by rudder_linear and rudder_linear_gelu_quant (the output

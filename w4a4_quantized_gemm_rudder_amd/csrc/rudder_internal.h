@@ -29,6 +29,14 @@ hipError_t launch_quant_act_dynamic(const uint16_t* X, const uint8_t* sid,
 
 size_t quant_act_workspace_bytes();
 
+// Dynamic mode with the library's own per-device scratch instead of a caller
+// workspace (no allocation on the call).
+hipError_t launch_quant_act_dynamic_noalloc(const uint16_t* X, const uint8_t* sid,
+                                            const float* inv_smooth, float* act_scale_out,
+                                            int M, int K, int S, int abits, int codes, void* Xq,
+                                            float* row_scale, hipStream_t stream);
+size_t quant_act_noalloc_scratch_bytes();
+
 hipError_t launch_linear(const void* Xq, const float* row_scale, const uint8_t* sid,
                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
                          const float* comp_b, int M, int N, int K, int S, int abits, int codes,

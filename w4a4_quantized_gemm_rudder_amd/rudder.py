@@ -35,7 +35,7 @@ MAX_STREAMS = 8
 
 EXPORTED = (
     "rudder_packed_weight_bytes", "rudder_packed_act_bytes", "rudder_quant_act_workspace_bytes",
-    "rudder_quantize_weights", "rudder_quant_act", "rudder_linear",
+    "rudder_quantize_weights", "rudder_quant_act", "rudder_quant_act_noalloc", "rudder_linear",
     "rudder_linear_gelu_quant", "rudder_gelu_bf16",
     "rudder_dequant_weights", "rudder_stream_sq_error_workspace_bytes", "rudder_stream_sq_error",
     "rudder_status_string", "rudder_last_error",
@@ -73,6 +73,8 @@ def load_library() -> ctypes.CDLL:
     lib.rudder_quantize_weights.restype = i
     lib.rudder_quant_act.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
     lib.rudder_quant_act.restype = i
+    lib.rudder_quant_act_noalloc.argtypes = [vp, vp, vp, vp, i, i, i, i, i, vp, vp, vp]
+    lib.rudder_quant_act_noalloc.restype = i
     lib.rudder_linear.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, vp, vp, vp]
     lib.rudder_linear.restype = i
     lib.rudder_linear_gelu_quant.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i,
@@ -164,6 +166,13 @@ def rudder_quant_act(X, stream_id, inv_smooth, act_scale, act_scale_out, workspa
     _check(load_library().rudder_quant_act(
         _ptr(X), _ptr(stream_id), _ptr(inv_smooth), _ptr(act_scale), _ptr(act_scale_out),
         _ptr(workspace), M, K, S, abits, codes, _ptr(Xq), _ptr(row_scale), _stream(stream)))
+
+
+def rudder_quant_act_noalloc(X, stream_id, inv_smooth, act_scale_out, M: int, K: int, S: int,
+                             abits: int, codes: int, Xq, row_scale, stream=None) -> None:
+    _check(load_library().rudder_quant_act_noalloc(
+        _ptr(X), _ptr(stream_id), _ptr(inv_smooth), _ptr(act_scale_out), M, K, S, abits, codes,
+        _ptr(Xq), _ptr(row_scale), _stream(stream)))
 
 
 def rudder_linear(Xq, row_scale, stream_id, Wq, w_scale, comp_a, comp_b,

@@ -7,10 +7,14 @@
 // scaling costs no extra launch and no intermediate HBM round trip (§1).
 //
 // gfx950 mapping
-//   * v_mfma_i32_32x32x32_i8: the MFMA "A" operand is a 32-channel slice of
-//     the weights (output channel n = MFMA row i), the "B" operand a 32-token
-//     slice of the activations (token m = MFMA column j), so each lane's
-//     accumulators hold one token row and runs of 4 consecutive channels.
+//   * The MFMA "A" operand is a slice of the weights (output channel n = MFMA
+//     row i), the "B" operand a slice of the activations (token m = MFMA
+//     column j), so each lane's accumulators hold token rows and runs of 4
+//     consecutive channels.  The W4A8 tiled loop runs
+//     v_mfma_i32_16x16x64_i8 (four per 32 x 32 fragment pair and 64 k; on
+//     these codes it sustains a higher rate than v_mfma_i32_32x32x32_i8 at
+//     the power-limited clock); W4A4 int codes and the weight-streaming
+//     kernel use v_mfma_i32_32x32x32_i8.
 //   * There is no int4 MFMA.  4-bit codes are widened in registers: the
 //     split-nibble word w becomes (w << 4) & 0xF0F0F0F0 and w & 0xF0F0F0F0,
 //     bytes equal to 16 * code in natural k order.  The int32 result is then
@@ -106,6 +110,13 @@ constexpr int kFmtD6 = 3;        // int8 activations as two E2M3 digit planes, E
 
 // The formats whose operands are E2M3 fields (fp32 accumulators).
 constexpr bool fp6_fmt(int fmt) { return fmt == kFmtF6 || fmt == kFmtD6; }
+
+// The W4A8 tiled loop runs v_mfma_i32_16x16x64_i8: on the layers' own codes
+// it sustains a higher rate than the 32x32x32 int8 shape at the
+// power-limited clock.  (int4 activations keep 32x32x32: their widening per
+// 16-token half costs more than the shape gains; the weight-streaming
+// kernel keeps 32x32x32 too.)
+constexpr bool i16_fmt(int fmt) { return fmt == kFmtA8; }
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef int v6i __attribute__((ext_vector_type(6)));
@@ -318,10 +329,60 @@ __device__ __forceinline__ void read_frag<v6i>(const uint8_t* block, int lane, v
     out = __builtin_shufflevector(p0, p1x, 0, 1, 2, 3, 4, 5);
 }
 
+// Accumulators of one 32-channel x 32-token fragment pair of the tiled
+// W4A8 loop: four 16 x 16 blocks of v_mfma_i32_16x16x64_i8.  Block b = 2 sc + st
+// covers channels 16 sc .. 16 sc + 15 and tokens 16 st .. 16 st + 15; lane l
+// holds token 16 st + l % 16 and channels 16 sc + 4 (l / 16) .. + 3, so
+// element 4 b + j of the fragment pair is channel j of that run of four.
+struct I16Acc {
+    v4i s[4];
+    __device__ __forceinline__ int operator[](int r) const { return s[r >> 2][r & 3]; }
+};
+template <int FMT>
+struct TileAcc {
+    typedef typename Fmt<FMT>::Acc type;
+};
+template <>
+struct TileAcc<kFmtA8> {
+    typedef I16Acc type;
+};
+
+__device__ __forceinline__ void zero_acc(v16f& a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = 0.0f;
+}
+__device__ __forceinline__ void zero_acc(v16i& a) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[r] = 0;
+}
+__device__ __forceinline__ void zero_acc(I16Acc& a) {
+#pragma unroll
+    for (int b = 0; b < 4; ++b) a.s[b] = v4i{0, 0, 0, 0};
+}
+// Scheduling fence on an accumulator (keeps the MFMAs that write it ahead of
+// what follows).
+__device__ __forceinline__ void pin(v16f& a) { asm volatile("" : "+v"(a)); }
+__device__ __forceinline__ void pin(v16i& a) { asm volatile("" : "+v"(a)); }
+__device__ __forceinline__ void pin(I16Acc& a) {
+    asm volatile("" : "+v"(a.s[0]), "+v"(a.s[1]), "+v"(a.s[2]), "+v"(a.s[3]));
+}
+
+// Byte offset, within the two consecutive 32-k code blocks (BLOCK bytes each,
+// SLOT bytes per 16-code slot) of a 64-k substep, of the 16 codes lane l
+// feeds to v_mfma_i32_16x16x64_i8 for rows 16 s .. 16 s + 15 of a 32-row
+// fragment: row 16 s + l % 16, k 16 (l / 16) .. + 15 of the substep, i.e.
+// block l / 32, slot (16 s + l % 16) + 32 ((l / 16) % 2).  Both operands use
+// this map, so every k of the substep pairs one weight and one activation
+// code whatever order the instruction sums them in.
+template <int SLOT, int BLOCK>
+__device__ __forceinline__ uint32_t i16_offset(int lane, int s) {
+    return (uint32_t)((lane >> 5) * BLOCK + (16 * s + (lane & 15) + 32 * ((lane >> 4) & 1)) * SLOT);
+}
+
 // Exact integer value of an accumulator element (the int8 path carries 16x
 // (W4A8) or 256x (W4A4) the true sum, see widen_nibbles).
-template <int FMT>
-__device__ __forceinline__ int acc_value(const typename Fmt<FMT>::Acc& a, int r) {
+template <int FMT, typename A>
+__device__ __forceinline__ int acc_value(const A& a, int r) {
     if constexpr (fp6_fmt(FMT)) return (int)a[r];
     else if constexpr (FMT == kFmtA8) return a[r] >> 4;
     else return a[r] >> 8;
@@ -329,8 +390,8 @@ __device__ __forceinline__ int acc_value(const typename Fmt<FMT>::Acc& a, int r)
 
 // The same value as an fp32 (exact: |acc| < 2^24).  The E2M3 accumulators
 // already hold it; the int containers shift and convert.
-template <int FMT>
-__device__ __forceinline__ float acc_float(const typename Fmt<FMT>::Acc& a, int r) {
+template <int FMT, typename A>
+__device__ __forceinline__ float acc_float(const A& a, int r) {
     if constexpr (fp6_fmt(FMT)) return a[r];
     else return (float)acc_value<FMT>(a, r);
 }
@@ -364,22 +425,26 @@ __device__ __forceinline__ void gemm_tile(
     const int ksteps = K / BK;
     const int n_tile0 = min(tile_n * TBN, N - 32);           // first channel of the tile (clamped)
 
-    // Stream id and row scale of this lane's FA token rows (plain loads; the
-    // compiler waits for them only in the epilogue).  The int formats fetch
-    // them before the main loop; the E2M3 loop has no registers to hold them
-    // across it, so it fetches them after the loop.
-    constexpr bool kLateRowData = fp6_fmt(FMT);
-    int row_stream[FA];
-    float row_rs[FA];
+    // Stream id and row scale of this lane's token rows (plain loads, issued
+    // after the main loop: holding them across it leaves the loop without
+    // registers).  A lane's accumulators cover one token per fragment (32x32
+    // shapes), or one token per 16-token half of it (W4A8, 16x16 blocks): TH
+    // token rows per fragment, token_of(th) within the fragment.
+    constexpr bool kI16 = i16_fmt(FMT);
+    constexpr int TH = kI16 ? 2 : 1;
+    auto token_of = [&](int th) { return kI16 ? 16 * th + (lane & 15) : (lane & 31); };
+    int row_stream[FA][TH];
+    float row_rs[FA][TH];
     auto fetch_row_data = [&]() {
 #pragma unroll
-        for (int g = 0; g < FA; ++g) {
-            const int mc = min(tile_m * BM + wm * (FA * 32) + g * 32 + (lane & 31), M - 1);
-            row_stream[g] = min(sid[mc] & (RUDDER_MAX_STREAMS - 1), S - 1);
-            row_rs[g] = row_scale[mc];
-        }
+        for (int g = 0; g < FA; ++g)
+#pragma unroll
+            for (int th = 0; th < TH; ++th) {
+                const int mc = min(tile_m * BM + wm * (FA * 32) + g * 32 + token_of(th), M - 1);
+                row_stream[g][th] = min(sid[mc] & (RUDDER_MAX_STREAMS - 1), S - 1);
+                row_rs[g][th] = row_scale[mc];
+            }
     };
-    if constexpr (!kLateRowData) fetch_row_data();
 
     // ---- epilogue tables -> LDS (one KiB per table row, one wave each) ----
     // row 0: w_scale, rows 1..S: comp_a[s], rows S+1..2S: comp_b[s] (and, when
@@ -436,13 +501,11 @@ __device__ __forceinline__ void gemm_tile(
             load_lds16(act_src[i] + a_off, voff, base + act_dst[i]);
     };
 
-    typename F::Acc acc[FW][FA];
+    typename TileAcc<FMT>::type acc[FW][FA];
 #pragma unroll
     for (int f = 0; f < FW; ++f)
 #pragma unroll
-        for (int g = 0; g < FA; ++g)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[f][g][r] = 0;
+        for (int g = 0; g < FA; ++g) zero_acc(acc[f][g]);
 
     // ---- main loop ----------------------------------------------------------
     // Weights straight from global memory into registers, activations
@@ -453,12 +516,18 @@ __device__ __forceinline__ void gemm_tile(
     // are issued, which gives a weight load two stages to land.  Activation
     // fragments are read one substep ahead into fa[j % 2] (substep j).
     static_assert(NS == 2, "direct-weight loop bookkeeping");
-    constexpr int P = BK / F::kKSub;                  // substeps per stage
+    // A substep is one MFMA k-step: 32 k (int4 activations), 64 k (E2M3, and
+    // the W4A8 16x16x64 shape, whose substep spans two 32-k code blocks).
+    // W4A8 takes a substep's activations in two planes, one per 16-token
+    // half of each fragment (the digit format's planes are its two digits).
+    constexpr int KS = kI16 ? 64 : F::kKSub;         // k per substep
+    constexpr int BPS = KS / F::kKSub;                // code blocks per substep
+    constexpr int P = BK / KS;                        // substeps per stage
     static_assert(P % 2 == 0, "substep parity");
     constexpr bool kF6 = fp6_fmt(FMT);
-    constexpr int PL = F::kPlanes;                    // activation planes per substep
-    constexpr int WL = kF6 ? 2 * FW : FW;             // weight loads per substep
-    typedef typename F::WFrag WOp;
+    constexpr int PL = kI16 ? 2 : F::kPlanes;         // activation planes per substep
+    constexpr int WL = (kF6 || kI16) ? 2 * FW : FW;   // weight loads per substep
+    typedef typename std::conditional<kI16, uint4, typename F::WFrag>::type WOp;
     typedef typename F::AFrag AOp;
     // this wave's weight block rows (wave-uniform: scalar bases; every lane
     // adds its own offsets)
@@ -469,13 +538,24 @@ __device__ __forceinline__ void gemm_tile(
         const int gnb = min(tile_n * (TBN / 32) + uwn * FW + f, nblocks - 1);
         wblk[f] = Wq + (size_t)gnb * kblocks * F::kWBlock;
     }
-    const uint32_t off0 = lane * (kF6 ? 16 : 8), off1 = 1024 + lane * 8;
+    // per-lane offsets: E2M3 plane 0 and plane 1; W4A8 the two 16-channel
+    // halves of a fragment (i16_offset)
+    // (the second half's offset is the first's plus 16 slots, a constant the
+    // load instructions take as an immediate)
+    const uint32_t off0 = kI16 ? i16_offset<8, 512>(lane, 0) : lane * (kF6 ? 16 : 8);
+    const uint32_t off1 = 1024 + lane * 8;
+    constexpr int kASlot = F::kABlock / 64;           // bytes of one 16-code slot
+    const uint32_t aoff0 = i16_offset<kASlot, F::kABlock>(lane, 0);
     auto load_w = [&](int kt, int kk, WOp (&dst)[FW], bool real = true) {
         const uint32_t o0 = real ? off0 : 0u, o1 = real ? off1 : 0u;
 #pragma unroll
         for (int f = 0; f < FW; ++f) {
-            const uint8_t* b = wblk[f] + (size_t)(kt * P + kk) * F::kWBlock;
-            if constexpr (kF6) {
+            const uint8_t* b = wblk[f] + (size_t)(kt * P + kk) * BPS * F::kWBlock;
+            if constexpr (kI16) {
+                const uint2 h0 = *reinterpret_cast<const uint2*>(b + o0);
+                const uint2 h1 = *reinterpret_cast<const uint2*>(b + o0 + 16 * 8);
+                dst[f] = make_uint4(h0.x, h0.y, h1.x, h1.y);
+            } else if constexpr (kF6) {
                 const v4i p0 = *reinterpret_cast<const v4i*>(b + o0);
                 const v2i p1 = *reinterpret_cast<const v2i*>(b + o1);
                 dst[f] = __builtin_shufflevector(
@@ -487,12 +567,22 @@ __device__ __forceinline__ void gemm_tile(
     };
     // js = kk * PL + plane: activation plane `plane` of substep kk
     auto read_acts = [&](int kt, int js, AOp (&dst)[FA]) {
-        int plane_off = 0;
-        if constexpr (PL > 1) plane_off = (js % PL) * F::kPlaneBytes;
-        const uint8_t* st =
-            lds + (kt % NS) * C::kStageBytes + (js / PL) * C::kActBlock + plane_off;
+        if constexpr (kI16) {
+            // plane js % 2: the 16-token half of every fragment
+            const uint8_t* st = lds + (kt % NS) * C::kStageBytes + (js / PL) * BPS * C::kActBlock;
+            const uint8_t* sa = st + aoff0 + (js % PL) * 16 * kASlot;
 #pragma unroll
-        for (int g = 0; g < FA; ++g) read_frag(st + (wm * FA + g) * C::kActPerMb, lane, dst[g]);
+            for (int g = 0; g < FA; ++g)
+                dst[g] = *reinterpret_cast<const AOp*>(sa + (wm * FA + g) * C::kActPerMb);
+        } else {
+            int plane_off = 0;
+            if constexpr (PL > 1) plane_off = (js % PL) * F::kPlaneBytes;
+            const uint8_t* st =
+                lds + (kt % NS) * C::kStageBytes + (js / PL) * C::kActBlock + plane_off;
+#pragma unroll
+            for (int g = 0; g < FA; ++g)
+                read_frag(st + (wm * FA + g) * C::kActPerMb, lane, dst[g]);
+        }
     };
     auto mma = [&](const WOp (&w)[FW], const AOp (&a)[FA], int first, int last, auto plane_) {
         constexpr int plane = decltype(plane_)::value;
@@ -508,19 +598,30 @@ __device__ __forceinline__ void gemm_tile(
                         acc[f][g] = mfma_scale_f32_32x32x64_fp6(
                             w[f], a[g], acc[f][g], 2, 2, F::kWeightScaleSel, F::kScaleWord, sel,
                             F::kScaleWord);
-            } else {
+            } else if constexpr (!kI16) {
                 if (f * FA + FA <= first || f * FA >= last) continue;
                 const v4i wf = widen_nibbles(w[f].x, w[f].y);
 #pragma unroll
                 for (int g = 0; g < FA; ++g) {
                     if (f * FA + g < first || f * FA + g >= last) continue;
-                    v4i af;
-                    if constexpr (FMT == kFmtA8)
-                        af = v4i{(int)a[g].x, (int)a[g].y, (int)a[g].z, (int)a[g].w};
-                    else
-                        af = widen_nibbles(a[g].x, a[g].y);
+                    const v4i af = widen_nibbles(a[g].x, a[g].y);
                     acc[f][g] =
                         __builtin_amdgcn_mfma_i32_32x32x32_i8(wf, af, acc[f][g], 0, 0, 0);
+                }
+            } else {
+                // plane = 16-token half st: blocks (sc, st) for both
+                // 16-channel halves sc of the weight fragment
+                if (f * FA + FA <= first || f * FA >= last) continue;
+                const v4i w0 = widen_nibbles(w[f].x, w[f].y);
+                const v4i w1 = widen_nibbles(w[f].z, w[f].w);
+#pragma unroll
+                for (int g = 0; g < FA; ++g) {
+                    if (f * FA + g < first || f * FA + g >= last) continue;
+                    const v4i af = v4i{(int)a[g].x, (int)a[g].y, (int)a[g].z, (int)a[g].w};
+                    acc[f][g].s[plane] =
+                        __builtin_amdgcn_mfma_i32_16x16x64_i8(w0, af, acc[f][g].s[plane], 0, 0, 0);
+                    acc[f][g].s[2 + plane] = __builtin_amdgcn_mfma_i32_16x16x64_i8(
+                        w1, af, acc[f][g].s[2 + plane], 0, 0, 0);
                 }
             }
         }
@@ -564,7 +665,7 @@ __device__ __forceinline__ void gemm_tile(
                 // landed, so the remaining MFMAs, issued after the next
                 // reads, carry no wait on those reads.
                 mma(wreg[u][kk], fa[js % 2], 0, 1, pl_);
-                asm volatile("" : "+v"(acc[0][0]));
+                pin(acc[0][0]);
                 __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
                 if (js + 1 < P * PL) {
                     read_acts(kt, js + 1, fa[(js + 1) % 2]);
@@ -583,7 +684,7 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
                 for (int f = 0; f < FW; ++f)
 #pragma unroll
-                    for (int g = 0; g < FA; ++g) asm volatile("" : "+v"(acc[f][g]));
+                    for (int g = 0; g < FA; ++g) pin(acc[f][g]);
             };
             plane_step(std::integral_constant<int, 0>{});
             if constexpr (PL > 1) plane_step(std::integral_constant<int, 1>{});
@@ -609,7 +710,7 @@ __device__ __forceinline__ void gemm_tile(
     constexpr int kWaveRowBytes = FW * 32 * 2;                 // 64, 128 or 256
     constexpr int kWaveRows = FA * 32;                         // 128 or 64
     constexpr int kRowChunks = kWaveRowBytes / 16;             // 4, 8 or 16
-    if constexpr (kLateRowData) fetch_row_data();
+    fetch_row_data();
     auto swz = [](int r) {
         return kRowChunks == 4 ? ((r >> 1) & 3) : (kRowChunks == 8 ? ((r >> 1) & 7) : (r & 15));
     };
@@ -618,24 +719,38 @@ __device__ __forceinline__ void gemm_tile(
     // next-layer quantizer (code epilogues): reciprocal step per row, Qa
     constexpr float kQNext = EPI == kEpiQ8 ? 127.0f : 7.0f;
     constexpr int kCodeRowBytes = FW * 32;                     // one byte per channel
-    float next_ia[FA];
+    float next_ia[FA][TH];
     if constexpr (EPI != kEpiBf16) {
 #pragma unroll
-        for (int g = 0; g < FA; ++g) next_ia[g] = step_reciprocal(nx.delta[row_stream[g]]);
+        for (int g = 0; g < FA; ++g)
+#pragma unroll
+            for (int th = 0; th < TH; ++th)
+                next_ia[g][th] = step_reciprocal(nx.delta[row_stream[g][th]]);
     }
     const int tab_shift = tile_n * TBN - (N >= BN ? min(n_tile0, N - BN) : 0);
     uint8_t* wstage = lds + wave * (kWaveRows * kWaveRowBytes);
     // When every token row of the wave belongs to one stream (the usual case:
     // rows come stream by stream), the comp rows a[s], b[s] are read once per
     // channel quad instead of once per 32-token block.
-    const int s_first = __builtin_amdgcn_readfirstlane(row_stream[0]);
+    const int s_first = __builtin_amdgcn_readfirstlane(row_stream[0][0]);
     bool one_stream = true;
 #pragma unroll
-    for (int g = 0; g < FA; ++g) one_stream = one_stream && row_stream[g] == s_first;
+    for (int g = 0; g < FA; ++g)
+#pragma unroll
+        for (int th = 0; th < TH; ++th) one_stream = one_stream && row_stream[g][th] == s_first;
     const bool wave_one_stream = __builtin_amdgcn_ballot_w64(!one_stream) == 0;
+    // Element 4 q + j of a fragment pair's accumulators is channel
+    // quad_ch(q) + j of the fragment and token row token_of(q_th(q)) of it:
+    // 32x32 shapes: channels 8 q + 4 (l / 32) .. + 3, token l % 32; int
+    // formats' 16x16 blocks (q = 2 sc + st): channels 16 sc + 4 (l / 16)
+    // .. + 3, token 16 st + l % 16.
+    auto quad_ch = [&](int q) {
+        return kI16 ? 16 * (q >> 1) + 4 * (lane >> 4) : 8 * q + 4 * (lane >> 5);
+    };
+    auto q_th = [&](int q) { return kI16 ? (q & 1) : 0; };
     // channel quad (f, q) of this lane, and its column in the table window
     auto table_col = [&](int f, int q) {
-        return min(wn * (FW * 32) + f * 32 + 8 * q + 4 * (lane >> 5) + tab_shift, 252);
+        return min(wn * (FW * 32) + f * 32 + quad_ch(q) + tab_shift, 252);
     };
     auto stage_tile = [&](auto uniform_) {
         constexpr bool kUniform = decltype(uniform_)::value;
@@ -660,11 +775,13 @@ __device__ __forceinline__ void gemm_tile(
         for (int f = 0; f < FW; ++f) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int nl = wn * (FW * 32) + f * 32 + 8 * q + 4 * (lane >> 5);  // in the tile
+                const int nl = wn * (FW * 32) + f * 32 + quad_ch(q);    // in the tile
                 const int ti = table_col(f, q);
                 const float4 ws =
                     kPreload ? pw[f][q] : *reinterpret_cast<const float4*>(tab + ti);
-                const int chunk = f * 4 + q;                       // 16-byte chunk in the wave row
+                const int ch = f * 32 + quad_ch(q);                // channel in the wave row
+                const int chunk = ch >> 3;                         // its 16-byte chunk
+                const int th = q_th(q);
                 if constexpr (kUniform && !kPreload) {
                     pa[f][q] = *reinterpret_cast<const float4*>(tab + 256 * (1 + s_first) + ti);
                     pb[f][q] =
@@ -672,8 +789,8 @@ __device__ __forceinline__ void gemm_tile(
                 }
 #pragma unroll
                 for (int g = 0; g < FA; ++g) {
-                    const int s = row_stream[g];
-                    const float rs = row_rs[g];
+                    const int s = row_stream[g][th];
+                    const float rs = row_rs[g][th];
                     float4 a, b;
                     if constexpr (kUniform) {
                         a = pa[f][q];
@@ -693,10 +810,10 @@ __device__ __forceinline__ void gemm_tile(
                     uint2 packed;
                     packed.x = pack_bf16x2_rne(y0, y1);
                     packed.y = pack_bf16x2_rne(y2, y3);
-                    const int r = g * 32 + (lane & 31);
+                    const int r = g * 32 + token_of(th);
                     if constexpr (EPI == kEpiBf16) {
                         *reinterpret_cast<uint2*>(wstage + r * kWaveRowBytes +
-                                                  ((chunk ^ swz(r)) * 16) + (lane >> 5) * 8) =
+                                                  ((chunk ^ swz(r)) * 16) + (ch & 4) * 2) =
                             packed;
                     } else {
                         // GELU of the bf16 values, then the next layer's quantizer:
@@ -707,7 +824,7 @@ __device__ __forceinline__ void gemm_tile(
                         const float g1 = bf16_bits_to_float(kGeluBf16[packed.x >> 16]);
                         const float g2 = bf16_bits_to_float(kGeluBf16[packed.y & 0xFFFFu]);
                         const float g3 = bf16_bits_to_float(kGeluBf16[packed.y >> 16]);
-                        const float ia = next_ia[g];
+                        const float ia = next_ia[g][th];
                         const uint32_t word =
                             ((uint32_t)quantize_clamped((g0 * ni.x) * ia, kQNext) & 0xFFu) |
                             (((uint32_t)quantize_clamped((g1 * ni.y) * ia, kQNext) & 0xFFu) << 8) |
@@ -716,9 +833,8 @@ __device__ __forceinline__ void gemm_tile(
                         // code staging: row r of the wave, 64 one-byte codes, 16-byte
                         // chunk k16 stored at chunk k16 ^ (r & 3)
                         *reinterpret_cast<uint32_t*>(
-                            wstage + r * kCodeRowBytes +
-                            (((f * 2 + (q >> 1)) ^ (r & 3)) * 16) + 8 * (q & 1) + 4 * (lane >> 5)) =
-                            word;
+                            wstage + r * kCodeRowBytes + ((((ch >> 4)) ^ (r & 3)) * 16) +
+                            (ch & 15)) = word;
                     }
                     if constexpr (ACC_OUT) {
                         const int m = tile_m * BM + wm * kWaveRows + r;
@@ -750,7 +866,7 @@ __device__ __forceinline__ void gemm_tile(
 #pragma unroll
             for (int g = 0; g < FA; ++g) {
                 const int m = m0 + g * 32 + lane;
-                if (m < M) nx.row_scale[m] = nx.delta[row_stream[g]];
+                if (m < M) nx.row_scale[m] = nx.delta[row_stream[g][kI16 ? (lane >> 4) & 1 : 0]];
             }
         }
         if (n0w >= N) return;

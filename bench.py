@@ -35,7 +35,8 @@ output, GELU kernel, quantizer) and fused (rudder_linear_gelu_quant).
 `small_m` reports action/proprio-sized calls (96 and 192 rows against
 full-width weights) as achieved HBM GB/s, timed as graph replays over
 rotating buffer sets that exceed the memory-side cache (and, for context, on
-one cache-resident set).  `calibration` times the offline search of one
+one cache-resident set), beside a plain device copy that moves the same
+bytes the same way.  `calibration` times the offline search of one
 layer's diagonal and layer-step table with the GPU in the loop.
 
 --workload picks another workload (each printed as one JSON line of the
@@ -529,6 +530,14 @@ def small_m_calls(torch, rudder, w4a4_codes: str, warm_reps: int = 20):
         warm = [0] * warm_reps
         res = {"gemm_cold": replay_us(cold, gemm), "pair_cold": replay_us(cold, pair),
                "gemm_warm": replay_us(warm, gemm), "pair_warm": replay_us(warm, pair)}
+        # reference: a plain device copy moving the same bytes (half read,
+        # half written) from the same number of rotating buffers, replayed
+        # the same way: what one launch of this size attains on this part
+        half = int(gemm_bytes // 2) // 16 * 16
+        copies = [(torch.empty(half, dtype=torch.uint8, device="cuda").fill_(1),
+                   torch.empty(half, dtype=torch.uint8, device="cuda")) for _ in range(n_sets)]
+        res["copy_cold"] = replay_us(cold, lambda i: copies[i][1].copy_(copies[i][0]))
+        del copies
         gbs = gemm_bytes / (res["gemm_cold"] * 1e-6) / 1e9
         gbs_w = gemm_bytes / (res["gemm_warm"] * 1e-6) / 1e9
         out[name] = {"M": M, "K": K, "N": N,
@@ -537,6 +546,7 @@ def small_m_calls(torch, rudder, w4a4_codes: str, warm_reps: int = 20):
                      "quant_act_plus_gemm_us": round(res["pair_cold"], 2),
                      "gemm_bytes": int(gemm_bytes), "gemm_GBps": round(gbs, 1),
                      "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                     "copy_same_bytes_us": round(res["copy_cold"], 2),
                      "buffer_sets": n_sets,
                      "buffer_set_MB": round(set_bytes / 1e6, 1),
                      "mall_warm": {"gemm_us": round(res["gemm_warm"], 2),

@@ -148,6 +148,25 @@ SMALL_M = [
     (192, 256, 16384, 3, 4, False, 31, CODES_E2M3),
     (250, 256, 16384, 3, 8, True, 32, CODES_INT),
     (60, 256, 16384, 2, 4, False, 33, CODES_INT),
+    # every workgroup shape the few-row launch chooses (rows per group x
+    # channels per workgroup), with channel counts that are odd multiples of
+    # 32 where the choice needs them
+    (193, 256, 2784, 3, 4, False, 80, CODES_INT),      # 64 x 96
+    (193, 256, 2208, 3, 4, True, 81, CODES_INT),       # 96 x 32
+    (193, 256, 4160, 3, 4, False, 82, CODES_INT),      # 96 x 64
+    (193, 256, 6240, 3, 4, False, 83, CODES_INT),      # 96 x 96
+    (97, 256, 4128, 3, 4, True, 84, CODES_INT),        # 128 x 32
+    (193, 256, 5504, 3, 4, False, 85, CODES_INT),      # 128 x 64
+    (193, 256, 2208, 3, 8, False, 86, CODES_INT),      # 64 x 96
+    (65, 256, 4128, 3, 8, True, 87, CODES_INT),        # 96 x 32
+    (193, 256, 4160, 3, 8, False, 88, CODES_INT),      # 96 x 64
+    (193, 256, 6240, 3, 8, False, 89, CODES_INT),      # 96 x 96
+    (193, 256, 2112, 3, 4, False, 90, CODES_E2M3),     # 64 x 64
+    (193, 256, 2208, 3, 4, True, 91, CODES_E2M3),      # 96 x 32
+    (193, 256, 6240, 3, 4, False, 92, CODES_E2M3),     # 96 x 96
+    (97, 256, 4128, 3, 4, False, 93, CODES_E2M3),      # 128 x 32
+    (193, 256, 5504, 3, 4, True, 94, CODES_E2M3),      # 128 x 64
+    (192, 4096, 12288, 3, 4, False, 95, CODES_E2M3),   # the benchmark's 192-row call
     # 8-bit codes as E2M3 digit planes (64-row groups only)
     (96, 2048, 6144, 3, 8, True, 34, CODES_E2M3),
     (192, 2048, 2048, 3, 8, False, 35, CODES_E2M3),

@@ -1141,7 +1141,7 @@ struct SkinnyChunk {
         NW * (fp6_fmt(FMT) ? 6 : 2) +
         FA * (FMT == kFmtD6 ? 12 : FMT == kFmtF6 ? 6 : (FMT == kFmtA8 ? 4 : 2));
     static constexpr int kFit = (200 - 16 * NW * FA) / (2 * kRegs);
-    static constexpr int D = NW == 1 ? (kRegs <= 12 ? 8 : (kRegs <= 24 ? 4 : 2))
+    static constexpr int D = NW == 1 ? (kRegs <= 12 ? 8 : (kRegs < 24 ? 4 : 2))
                                      : (kFit >= 8 ? 8 : kFit >= 4 ? 4 : kFit >= 2 ? 2 : 1);
 };
 
@@ -1335,25 +1335,18 @@ __global__ __launch_bounds__(kSkinnyThreads, 1) void w4_skinny_kernel(
 }
 int device_cus();
 
-// NW = 2 (64 channels per workgroup) halves the activation re-reads, which
-// dominate the L2 traffic of this kernel, whenever the grid still covers
-// every compute unit.
-template <int FMT, int FA, bool ACC_OUT>
+// One launch of the weight-streaming kernel with FA * 32-row groups and NW
+// 32-channel blocks per workgroup.
+template <int FMT, int FA, int NW, bool ACC_OUT>
 hipError_t launch_skinny(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                          const uint8_t* Wq, const float* w_scale, const float* comp_a,
                          const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                          int32_t* acc_out, hipStream_t stream) {
     const unsigned row_groups = (unsigned)((M + FA * 32 - 1) / (FA * 32));
-    if (N % 64 == 0 && (N / 64) * (int)row_groups >= device_cus())
-        hipLaunchKernelGGL((w4_skinny_kernel<FMT, FA, 2, ACC_OUT>),
-                           dim3((unsigned)(N / 64), row_groups), dim3(kSkinnyThreads), 0, stream,
-                           xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S, Y,
-                           acc_out);
-    else
-        hipLaunchKernelGGL((w4_skinny_kernel<FMT, FA, 1, ACC_OUT>),
-                           dim3((unsigned)(N / 32), row_groups), dim3(kSkinnyThreads), 0, stream,
-                           xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S, Y,
-                           acc_out);
+    hipLaunchKernelGGL((w4_skinny_kernel<FMT, FA, NW, ACC_OUT>),
+                       dim3((unsigned)(N / (32 * NW)), row_groups), dim3(kSkinnyThreads), 0,
+                       stream, xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K, S, Y,
+                       acc_out);
     return hipGetLastError();
 }
 
@@ -1417,26 +1410,65 @@ int device_cus() {
     return cus[dev];
 }
 
+// Workgroup shape of the weight-streaming kernel: FA * 32-row groups and NW
+// 32-channel blocks per workgroup, one 8-wave workgroup per compute unit at
+// a time.  Every workgroup reads its weight slice and its rows' activation
+// codes in full, so the time follows the operand bytes on the busiest
+// compute unit: rounds of workgroups x (weight bytes + activation bytes of
+// one workgroup).  The shape minimizing that is taken, the fewest rows and
+// then the fewest channels on a tie.  (Measured on six few-row layer shapes,
+// 32..250 rows x 2048..16384 channels, this picks the fastest shape in each;
+// the 96-channel, 128-row shape runs out of registers and is not offered.)
+// The digit format keeps 64-row groups: its two activation planes per
+// fragment leave no registers for more.
+template <int FMT>
+void skinny_shape(int M, int N, int& fa, int& nw) {
+    using F = Fmt<FMT>;
+    const double w = (double)F::kWBlock / (32.0 * F::kKSub);   // bytes per weight code
+    const double a = (double)F::kABlock / (32.0 * F::kKSub);   // bytes per activation code
+    const long cus = device_cus();
+    double best = 1e300;
+    fa = 2;
+    nw = 1;
+    for (int f = 2; f <= (FMT == kFmtD6 ? 2 : 4); ++f) {
+        for (int n = 1; n <= (FMT == kFmtD6 ? 2 : 3); ++n) {
+            if (f * n > 9 || N % (32 * n)) continue;
+            const long groups = (M + 32 * f - 1) / (32 * f);
+            const long wgs = (long)(N / (32 * n)) * groups;
+            const long rounds = (wgs + cus - 1) / cus;
+            const double bytes = rounds * (32.0 * n * w + (double)min(M, 32 * f) * a);
+            if (bytes < best * (1.0 - 1e-9)) {
+                best = bytes;
+                fa = f;
+                nw = n;
+            }
+        }
+    }
+}
+
 template <int FMT, bool ACC_OUT>
 hipError_t launch_small(const uint8_t* xq, const float* row_scale, const uint8_t* sid,
                         const uint8_t* Wq, const float* w_scale, const float* comp_a,
                         const float* comp_b, int M, int N, int K, int S, uint16_t* Y,
                         int32_t* acc_out, hipStream_t stream) {
-    // 64-row groups for few rows, and when several 128-row groups would
-    // still leave compute units idle (the 192-row remainder of a 2048-wide
-    // layer: 128 workgroups of 128 rows, 192 of 64); always for the digit
-    // format, whose two activation planes per fragment leave no registers
-    // for 128-row groups
-    if constexpr (FMT == kFmtD6) {
-        return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
-                                              M, N, K, S, Y, acc_out, stream);
-    } else {
-        if (M <= 64 || (M > 128 && (N / 32) * ((M + 127) / 128) < device_cus()))
-            return launch_skinny<FMT, 2, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,
-                                                  comp_b, M, N, K, S, Y, acc_out, stream);
-        return launch_skinny<FMT, 4, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b,
-                                              M, N, K, S, Y, acc_out, stream);
+    int fa, nw;
+    skinny_shape<FMT>(M, N, fa, nw);
+#define RUDDER_SKINNY(FA_, NW_)                                                                \
+    if (fa == FA_ && nw == NW_)                                                                \
+        return launch_skinny<FMT, FA_, NW_, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a,  \
+                                                     comp_b, M, N, K, S, Y, acc_out, stream);
+    RUDDER_SKINNY(2, 1)
+    RUDDER_SKINNY(2, 2)
+    if constexpr (FMT != kFmtD6) {
+        RUDDER_SKINNY(2, 3)
+        RUDDER_SKINNY(3, 1)
+        RUDDER_SKINNY(3, 2)
+        RUDDER_SKINNY(3, 3)
+        RUDDER_SKINNY(4, 1)
+        RUDDER_SKINNY(4, 2)
     }
+#undef RUDDER_SKINNY
+    return hipErrorInvalidValue;          // not reached: skinny_shape offers only the above
 }
 
 // The tiled kernel's LDS ring holds two stages of activation codes.

@@ -334,6 +334,47 @@ def test_m0_is_noop_on_device():
     assert int((Y != 7).sum()) == 0
 
 
+@pytest.mark.parametrize("abits,codes", [(8, CODES_INT), (4, CODES_E2M3)])
+def test_linear_row_scales_varying_within_a_stream(abits, codes):
+    """rudder_linear takes any row scales: rows of one stream whose scales
+    differ (some waves with one stream and one scale, some with one stream
+    and several, a -0.0 scale beside +0.0) must match the oracle's
+    epilogue on the same integer accumulators."""
+    import torch
+    from w4a4_quantized_gemm_rudder_amd import rudder
+    log(f"case varying row scales abits={abits} codes={codes}")
+    rng = np.random.default_rng(500 + abits)
+    M, K, N, S = 640, 256, 512, 2
+    x = rng.standard_normal((M, K))
+    X = _torch_bf16_bits(x)
+    Wb = _torch_bf16_bits(rng.standard_normal((K, N)) * 0.02)
+    sid = np.zeros(M, np.uint8)
+    sid[384:] = 1
+    s = np.ones(K, np.float32)
+    a = rng.uniform(0.9, 1.1, (S, N)).astype(np.float32)
+    b = (rng.standard_normal((S, N)) * 0.01).astype(np.float32)
+    b[:, :8] = -0.0
+    run = LayerRun(X, sid, Wb, s, a, b, S, abits, codes)
+    qa_max = 127 if abits == 8 else 7
+    delta = (np.full(S, np.abs(x).max() / qa_max)).astype(np.float32)
+    Xq, _ = run.r.quant_act(run.X, run.sid_d, run.inv_smooth, to_dev(delta), S, abits, codes)
+    rs = delta[sid].copy()
+    rs[130:140] *= np.float32(1.5)       # a wave of one stream, several scales
+    rs[200] = np.float32(-0.0)           # -0.0 among +0.0 rows
+    rs[201:256] = np.float32(0.0)
+    rs[512:] = np.float32(0.75) * rs[512:]
+    Y, acc = run.r.linear(Xq, to_dev(rs), run.sid_d, run.Wq, run.w_scale, to_dev(a), to_dev(b),
+                          M, N, K, S, abits, codes, acc_out=True)
+    torch.cuda.synchronize()
+    import oracle
+    from gpu_harness import assert_y_close, bf16_to_host_bits
+    qa, _ = oracle.quant_act(X, sid, run.o_inv, delta, S, abits)
+    o_acc = oracle.int_gemm(qa, run.o_qw)
+    o_Y = oracle.epilogue(o_acc, rs, sid, run.o_ws, a, b)
+    assert np.array_equal(acc.cpu().numpy(), o_acc)
+    log(f"  {assert_y_close('Y', bf16_to_host_bits(Y), o_Y)}")
+
+
 # ---------------------------------------------------------------------------
 # Full-size workloads (the launch configuration the benchmark times), in
 # every code container the benchmark can run them in.  Codes and row scales

@@ -200,6 +200,16 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     (8448, 128, 2048, 3, 8, False, 58, CODES_INT),
     (8448, 256, 2048, 2, 4, True, 59, CODES_E2M3),
     (8449, 128, 2048, 3, 4, False, 60, CODES_INT),
+    # less than one round but more tiles than compute units: 4192 rows x 2048
+    # channels (264 tiles, 256 CUs) take 4096 rows as one tile per CU and
+    # stream the other 96; 2200 x 4096 (288 tiles) streams 152 rows; a
+    # 256-row remainder (the most streamed) and 257 (not streamed)
+    (4192, 256, 2048, 3, 8, False, 61, CODES_INT),
+    (4192, 512, 2048, 2, 4, True, 62, CODES_E2M3),
+    (2200, 128, 4096, 3, 4, False, 63, CODES_INT),
+    (2200, 256, 4096, 3, 8, False, 64, CODES_E2M3),
+    (4352, 128, 2048, 3, 8, False, 65, CODES_INT),
+    (4353, 256, 2048, 3, 4, False, 66, CODES_E2M3),
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")

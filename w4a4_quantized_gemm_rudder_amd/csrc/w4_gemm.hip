@@ -1528,6 +1528,22 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
                                               N, K, S, Y, acc_out, stream, NextLayerQuant{},
                                               m_main);
     }
+    // Less than one round, but more tiles than compute units: the few CUs
+    // that get a second tile set the launch time (two co-resident tiles take
+    // longer than a lone one), while the rest hold one.  When the rows past
+    // one tile per CU are few, the tiles take the rows that give each CU at
+    // most one, and the streaming blocks take the rest in the free second
+    // slots, running beside the tiles.
+    const int cus = device_cus();
+    if (full == 0 && tiles > cus && per_cu >= kBlocksPerCU) {
+        const int m_main = (cus / tiles_n) * BM;
+        const int tail = M - m_main;
+        const int groups = (tail + 127) / 128;
+        if (m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && groups * N <= kSplitMaxWidth)
+            return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
+                                              N, K, S, Y, acc_out, stream, NextLayerQuant{}, 0,
+                                              m_main);
+    }
     return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,
                                       S, Y, acc_out, stream);
 }

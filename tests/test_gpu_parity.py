@@ -210,6 +210,10 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     (2200, 256, 4096, 3, 8, False, 64, CODES_E2M3),
     (4352, 128, 2048, 3, 8, False, 65, CODES_INT),
     (4353, 256, 2048, 3, 4, False, 66, CODES_E2M3),
+    # a full round, then more tiles than CUs (4192 x 6144: 792 tiles): the
+    # first 4096 rows as tiles (one round plus one per CU), 96 rows streamed
+    (4192, 256, 6144, 3, 8, False, 67, CODES_INT),
+    (4192, 128, 6144, 2, 4, True, 68, CODES_E2M3),
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")
@@ -226,6 +230,9 @@ def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     (8384, 256, 6144, 3, 4, True, 45, CODES_INT),
     (8292, 128, 12288, 4, 8, False, 46, CODES_INT),
     (8384, 128, 8128, 3, 8, False, 47, CODES_INT),      # last narrow tile half outside N
+    # 2100 x 12288 (816 tiles): one round plus one tile per CU, then 52 rows
+    # as half-width tiles
+    (2100, 128, 12288, 3, 8, False, 69, CODES_INT),
 ])
 def test_round_remainder_narrow_tiles(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case narrow tail M={M} K={K} N={N} S={S} abits={abits} codes={codes}")

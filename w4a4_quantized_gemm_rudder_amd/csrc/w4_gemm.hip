@@ -1513,8 +1513,19 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
     const int per_cu = (int)((160 * 1024) / Cfg<FMT, kRing>::lds_bytes(S));
     const int slots = device_cus() * (per_cu < kBlocksPerCU ? per_cu : kBlocksPerCU);
     const int full = slots > 0 ? tiles / slots : 0;
-    if (full >= 1 && tiles % slots != 0) {
-        const int m_main = (full * slots / tiles_n) * BM;
+    const int rem = tiles - full * slots;
+    // The tiles that run as full tiles: whole rounds, and then at most one
+    // more per compute unit.  A partial round with more tiles than compute
+    // units puts two co-resident tiles on a few of them, and those set the
+    // launch time (a lone tile takes well under the time of two together);
+    // the rows past one tile per CU then go to the streaming blocks or
+    // half-width tiles below, which fill the free second slots beside the
+    // lone tiles.
+    const int cus = device_cus();
+    const bool pairs_in_last = rem > cus && per_cu >= kBlocksPerCU;
+    const int lead = full * slots + (pairs_in_last ? cus : 0);
+    if (rem != 0 && lead > 0) {
+        const int m_main = (lead / tiles_n) * BM;
         const int tail = M - m_main;
         const int groups = (tail + 127) / 128;
         if (m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && groups * N <= kSplitMaxWidth)
@@ -1526,22 +1537,6 @@ hipError_t launch_fmt(const uint8_t* xq, const float* row_scale, const uint8_t* 
         if (!fp6_fmt(FMT) && m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && N >= BN)
             return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
                                               N, K, S, Y, acc_out, stream, NextLayerQuant{},
-                                              m_main);
-    }
-    // Less than one round, but more tiles than compute units: the few CUs
-    // that get a second tile set the launch time (two co-resident tiles take
-    // longer than a lone one), while the rest hold one.  When the rows past
-    // one tile per CU are few, the tiles take the rows that give each CU at
-    // most one, and the streaming blocks take the rest in the free second
-    // slots, running beside the tiles.
-    const int cus = device_cus();
-    if (full == 0 && tiles > cus && per_cu >= kBlocksPerCU) {
-        const int m_main = (cus / tiles_n) * BM;
-        const int tail = M - m_main;
-        const int groups = (tail + 127) / 128;
-        if (m_main > 0 && tail > 0 && tail <= kSkinnyMaxM && groups * N <= kSplitMaxWidth)
-            return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M,
-                                              N, K, S, Y, acc_out, stream, NextLayerQuant{}, 0,
                                               m_main);
     }
     return launch_tiled<FMT, ACC_OUT>(xq, row_scale, sid, Wq, w_scale, comp_a, comp_b, M, N, K,

@@ -964,7 +964,7 @@ __device__ __forceinline__ void skinny_tile(
 // them in the same launch, which the compute units pick up as the full
 // tiles drain:
 //   - narrow layers (bf16 output): blocks from tail_first on cover rows
-//     tail_m0 .. M - 1 as streaming blocks of 64 rows x 32 channels (the
+//     tail_m0 .. M - 1 as streaming blocks of tail_fa * 32 rows x 32 channels (the
 //     weight-streaming kernel's work, its four waves splitting k);
 //   - wider layers, int containers (bf16 output): blocks from narrow_first
 //     on cover rows narrow_m0 .. M - 1 as tiles of BN / 2 channels, twice as
@@ -978,7 +978,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
     int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, int narrow_first, int narrow_m0,
-    int touch_blocks, int tail_first, int tail_m0, NextLayerQuant nx) {
+    int touch_blocks, int tail_first, int tail_m0, int tail_fa, NextLayerQuant nx) {
     if ((int)blockIdx.x < touch_blocks) {
         const size_t bytes = fp6_fmt(FMT) ? (size_t)N * K * 3 / 4 : (size_t)N * K / 2;
         const size_t lines = bytes / 128;
@@ -998,6 +998,15 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
             const int t = bid - tail_first;
             const int cbs = N / 32;
             const size_t a_off = (size_t)(tail_m0 / 32) * (K / F::kKSub) * F::kABlock;
+            if constexpr (FMT != kFmtD6) {
+                if (tail_fa == 3) {
+                    skinny_tile<FMT, 3, 1, ACC_OUT, kWaves>(
+                        Xq + a_off, row_scale + tail_m0, sid + tail_m0, Wq, w_scale, comp_a,
+                        comp_b, M - tail_m0, N, K, S, Y + (size_t)tail_m0 * N,
+                        ACC_OUT ? acc_out + (size_t)tail_m0 * N : acc_out, t % cbs, t / cbs, lds);
+                    return;
+                }
+            }
             skinny_tile<FMT, 2, 1, ACC_OUT, kWaves>(
                 Xq + a_off, row_scale + tail_m0, sid + tail_m0, Wq, w_scale, comp_a, comp_b,
                 M - tail_m0, N, K, S, Y + (size_t)tail_m0 * N,
@@ -1350,6 +1359,33 @@ hipError_t launch_skinny(const uint8_t* xq, const float* row_scale, const uint8_
     return hipGetLastError();
 }
 
+// Rows per streaming block (in 32-row groups: 2 or 3) for the rows past the
+// tiles of a tiled launch.  Each block reads its 32 channels' weights and its
+// rows' activation codes in full, and blocks sharing a compute unit share its
+// bandwidth, so the time follows (blocks per CU, rounded up) x (bytes of one
+// block); the smaller is taken, 64-row groups on a tie.  The digit format
+// keeps 64-row groups (registers).
+template <int FMT>
+int tail_rows_per_block(int rows, int N, int K) {
+    using F = Fmt<FMT>;
+    if (FMT == kFmtD6) return 2;
+    const double w = (double)F::kWBlock / (32.0 * F::kKSub);   // bytes per weight code
+    const double a = (double)F::kABlock / (32.0 * F::kKSub);   // bytes per activation code
+    const long cus = device_cus();
+    int best_f = 2;
+    double best = 1e300;
+    for (int f = 2; f <= 3; ++f) {
+        const long blocks = (long)((rows + 32 * f - 1) / (32 * f)) * (N / 32);
+        const long per_cu = (blocks + cus - 1) / cus;
+        const double bytes = per_cu * (32.0 * K * w + (double)min(rows, 32 * f) * K * a);
+        if (bytes < best * (1.0 - 1e-9)) {
+            best = bytes;
+            best_f = f;
+        }
+    }
+    return best_f;
+}
+
 // split_m > 0 (int containers, bf16 output): rows split_m .. M - 1 run as
 // narrow tiles in the same launch; tail_m0 > 0 (bf16 output): rows
 // tail_m0 .. M - 1 run as streaming blocks in the same launch (see
@@ -1362,7 +1398,9 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
                           const NextLayerQuant& nx = NextLayerQuant{}, int split_m = 0,
                           int tail_m0 = 0) {
     using C = Cfg<FMT, NS>;
-    static_assert(SkinnySmem<2, 1>::kBytes <= C::lds_bytes(1), "streaming blocks' LDS");
+    static_assert(SkinnySmem<2, 1>::kBytes <= C::lds_bytes(1) &&
+                      SkinnySmem<3, 1>::kBytes <= C::lds_bytes(1),
+                  "streaming blocks' LDS");
     constexpr int kExtra = EPI != kEpiBf16 ? 1 : 0;
     static_assert(C::lds_bytes(1, kExtra) <= kLdsLimit, "LDS budget");
     static_assert(EPI == kEpiBf16 || Waves<FMT>::FW == 2, "code epilogue: 64 channels per wave");
@@ -1381,7 +1419,9 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
     const int main_tiles = tiles_m * tiles_n;
     const int narrow_tiles =
         split ? ((M - split_m + BM - 1) / BM) * ((N + BN / 2 - 1) / (BN / 2)) : 0;
-    const int tail_blocks = tail ? ((M - tail_m0 + 63) / 64) * (N / 32) : 0;
+    const int tail_fa = tail ? tail_rows_per_block<FMT>(M - tail_m0, N, K) : 2;
+    const int tail_blocks =
+        tail ? ((M - tail_m0 + 32 * tail_fa - 1) / (32 * tail_fa)) * (N / 32) : 0;
     // weight touch blocks (few-row launches read the weights only once or
     // twice and go without)
     const int touch_blocks = M > kSkinnyMaxM ? kTouchBlocks : 0;
@@ -1391,7 +1431,8 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
                        C::lds_bytes(S, kExtra), stream, xq, row_scale, sid, Wq, w_scale, comp_a,
                        comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n, main_tiles,
                        split ? split_m : M, touch_blocks,
-                       tail ? main_tiles + narrow_tiles : 0x7FFFFFFF, tail ? tail_m0 : M, nx);
+                       tail ? main_tiles + narrow_tiles : 0x7FFFFFFF, tail ? tail_m0 : M,
+                       tail_fa, nx);
     return hipGetLastError();
 }
 

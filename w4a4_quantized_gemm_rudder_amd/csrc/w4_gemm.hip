@@ -978,8 +978,7 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
     const float* __restrict__ w_scale, const float* __restrict__ comp_a,
     const float* __restrict__ comp_b, int M, int N, int K, int S, uint16_t* __restrict__ Y,
     int32_t* __restrict__ acc_out, int tiles_m, int tiles_n, int narrow_first, int narrow_m0,
-    int touch_blocks, int tail_first, int tail_m0, int tail_fa, size_t touch_act_bytes,
-    NextLayerQuant nx) {
+    int touch_blocks, int tail_first, int tail_m0, int tail_fa, NextLayerQuant nx) {
     if ((int)blockIdx.x < touch_blocks) {
         const size_t bytes = fp6_fmt(FMT) ? (size_t)N * K * 3 / 4 : (size_t)N * K / 2;
         const size_t lines = bytes / 128;
@@ -988,11 +987,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
         for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < lines;
              i += (size_t)touch_blocks * kThreads)
             v ^= p[i * 32];
-        // then the activation codes' lines, when the launch asks for it
-        const uint32_t* q = reinterpret_cast<const uint32_t*>(Xq);
-        for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < touch_act_bytes / 128;
-             i += (size_t)touch_blocks * kThreads)
-            v ^= q[i * 32];
         asm volatile("" ::"v"(v));          // the loads are the point; the data is not used
         return;
     }
@@ -1052,7 +1046,6 @@ __global__ __launch_bounds__(kThreads, kBlocksPerCU) void w4_gemm_kernel(
 constexpr int kSkinnyWaves = 8;
 constexpr int kSkinnyMaxM = 256;                 // rows handled by the small-M kernel
 constexpr int kTouchBlocks = 64;                 // weight touch blocks of a tiled launch
-constexpr size_t kTouchActMax = 32u << 20;        // most activation-code bytes touched
 constexpr int kSplitMaxWidth = 8192;             // see launch_fmt
 constexpr int kSkinnyThreads = 64 * kSkinnyWaves;
 
@@ -1432,21 +1425,6 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
     // weight touch blocks (few-row launches read the weights only once or
     // twice and go without)
     const int touch_blocks = M > kSkinnyMaxM ? kTouchBlocks : 0;
-    // The E2M3 quantizers stream their codes past the caches, so these
-    // launches find their activation codes in HBM; the touch blocks then
-    // touch those too, when they are few (at most kTouchActMax bytes: more
-    // keeps the touch blocks busy for long and no longer stays in the
-    // memory-side cache until it is read), and unless the launch is about
-    // one round of tiles: there the tiles held back behind the longer touch
-    // blocks end last and set the launch time.  With more than a round, or
-    // with free slots beside everything, the touch costs little.
-    const size_t act_bytes = (size_t)((M + 31) / 32) * (K / C::F::kKSub) * C::F::kABlock;
-    const int per_cu = (int)((160 * 1024) / C::lds_bytes(S, kExtra));
-    const int slots = device_cus() * (per_cu < kBlocksPerCU ? per_cu : kBlocksPerCU);
-    const int work = main_tiles + narrow_tiles + tail_blocks;
-    const bool touch_acts = fp6_fmt(FMT) && touch_blocks > 0 && act_bytes <= kTouchActMax &&
-                            (main_tiles > slots || work <= slots - touch_blocks);
-    const size_t touch_act_bytes = touch_acts ? act_bytes : 0;
     hipLaunchKernelGGL((w4_gemm_kernel<FMT, NS, ACC_OUT, EPI>),
                        dim3((unsigned)(touch_blocks + main_tiles + narrow_tiles + tail_blocks)),
                        dim3(kThreads),
@@ -1454,7 +1432,7 @@ hipError_t launch_variant(const uint8_t* xq, const float* row_scale, const uint8
                        comp_b, M, N, K, S, Y, acc_out, tiles_m, tiles_n, main_tiles,
                        split ? split_m : M, touch_blocks,
                        tail ? main_tiles + narrow_tiles : 0x7FFFFFFF, tail ? tail_m0 : M,
-                       tail_fa, touch_act_bytes, nx);
+                       tail_fa, nx);
     return hipGetLastError();
 }
 

@@ -21,14 +21,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxPartials = 1024;          // dynamic-mode partial-absmax blocks
 
-// Code stores with the streaming (non-temporal) hint.
-__device__ __forceinline__ void nt_store16(uint8_t* p, uint4 v) {
-    typedef unsigned v4u __attribute__((ext_vector_type(4)));
-    __builtin_nontemporal_store(v4u{v.x, v.y, v.z, v.w}, reinterpret_cast<v4u*>(p));
+// Code stores of the E2M3 codec (16- and 8-byte pieces of a code block).
+__device__ __forceinline__ void store16(uint8_t* p, uint4 v) {
+    *reinterpret_cast<uint4*>(p) = v;
 }
-__device__ __forceinline__ void nt_store8(uint8_t* p, uint2 v) {
-    typedef unsigned v2u __attribute__((ext_vector_type(2)));
-    __builtin_nontemporal_store(v2u{v.x, v.y}, reinterpret_cast<v2u*>(p));
+__device__ __forceinline__ void store8(uint8_t* p, uint2 v) {
+    *reinterpret_cast<uint2*>(p) = v;
 }
 
 // 16 consecutive floats at a wave-uniform, 16-byte-aligned address, held in
@@ -267,9 +265,9 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
 #pragma unroll
         for (int i = 0; i < 32; ++i) c[i] = 0.0f;
     }
-    // Streaming stores: the E2M3 GEMM that reads these codes runs 2-3%
-    // faster than after write-back stores (the int codecs' GEMMs run
-    // slower, and those codecs keep plain stores).
+    // Write-back stores: the codes then sit in the caches when the GEMM
+    // that reads them starts (with streaming stores it found them in HBM,
+    // and the 8192-deep down-projection ran 14% slower).
     const int slot = e2m3_slot(r, k0);
     if constexpr (ABITS == 8) {
         float ch[32], cl[32];
@@ -285,16 +283,16 @@ __global__ __launch_bounds__(kThreads) void quant_act_e2m3_kernel(
         pack_e2m3x32(ch, dh);
         pack_e2m3x32(cl, dl);
         uint8_t* blk = Xq + 2 * e2m3_block_offset(r, k0, K);
-        nt_store16(blk + slot * 16, make_uint4(dh[0], dh[1], dh[2], dh[3]));
-        nt_store8(blk + 1024 + slot * 8, make_uint2(dh[4], dh[5]));
-        nt_store16(blk + 1536 + slot * 16, make_uint4(dl[0], dl[1], dl[2], dl[3]));
-        nt_store8(blk + 1536 + 1024 + slot * 8, make_uint2(dl[4], dl[5]));
+        store16(blk + slot * 16, make_uint4(dh[0], dh[1], dh[2], dh[3]));
+        store8(blk + 1024 + slot * 8, make_uint2(dh[4], dh[5]));
+        store16(blk + 1536 + slot * 16, make_uint4(dl[0], dl[1], dl[2], dl[3]));
+        store8(blk + 1536 + 1024 + slot * 8, make_uint2(dl[4], dl[5]));
     } else {
         uint32_t d[6];
         pack_e2m3x32(c, d);
         uint8_t* blk = Xq + e2m3_block_offset(r, k0, K);
-        nt_store16(blk + slot * 16, make_uint4(d[0], d[1], d[2], d[3]));
-        nt_store8(blk + 1024 + slot * 8, make_uint2(d[4], d[5]));
+        store16(blk + slot * 16, make_uint4(d[0], d[1], d[2], d[3]));
+        store8(blk + 1024 + slot * 8, make_uint2(d[4], d[5]));
     }
 }
 

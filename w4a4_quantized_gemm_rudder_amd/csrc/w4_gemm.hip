@@ -34,8 +34,10 @@
 //     so every HBM line is written once.
 //   * Ragged last round: when the rows spill a little past a whole number of
 //     tile rounds, those rows run in the same launch, after the tiles: as
-//     weight-streaming blocks for narrow layers, as half-width tiles for
-//     wider ones (int containers).
+//     weight-streaming blocks (64 or 96 rows each) for narrow layers, as
+//     half-width tiles for wider ones (int containers).  A partial round
+//     with more tiles than compute units keeps one tile per CU and hands
+//     the remaining rows to those forms.
 //   * Weight touch: a few leading blocks of each launch read the packed
 //     weights once, line by line, so that the tiles' many re-reads of them
 //     hit the memory-side cache instead of HBM.

@@ -214,6 +214,10 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     # first 4096 rows as tiles (one round plus one per CU), 96 rows streamed
     (4192, 256, 6144, 3, 8, False, 67, CODES_INT),
     (4192, 128, 6144, 2, 4, True, 68, CODES_E2M3),
+    # eight streams: the epilogue tables leave one workgroup per CU, so a
+    # round is 256 tiles and the 96 rows past it stream after the tiles
+    (4192, 256, 2048, 8, 4, False, 70, CODES_E2M3),
+    (4192, 128, 2048, 8, 8, True, 71, CODES_INT),
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")

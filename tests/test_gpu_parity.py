@@ -218,6 +218,9 @@ def test_small_m(M, K, N, S, abits, dynamic, seed, codes):
     # round is 256 tiles and the 96 rows past it stream after the tiles
     (4192, 256, 2048, 8, 4, False, 70, CODES_E2M3),
     (4192, 128, 2048, 8, 8, True, 71, CODES_INT),
+    # the same 2100 x 4128 in the E2M3 container: no half-width tiles, so all
+    # 289 tiles run (a partial round), the last column 32 channels wide
+    (2100, 256, 4128, 2, 4, True, 97, CODES_E2M3),
 ])
 def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case round split M={M} K={K} N={N} S={S} abits={abits} codes={codes}")
@@ -237,6 +240,10 @@ def test_round_remainder_split(M, K, N, S, abits, dynamic, seed, codes):
     # 2100 x 12288 (816 tiles): one round plus one tile per CU, then 52 rows
     # as half-width tiles
     (2100, 128, 12288, 3, 8, False, 69, CODES_INT),
+    # 2100 x 4128 (17 tile columns, the last 32 channels wide; 289 tiles):
+    # one tile per CU over 1920 rows, then 180 rows as half-width tiles,
+    # whose last column is mostly past N
+    (2100, 128, 4128, 3, 8, False, 96, CODES_INT),
 ])
 def test_round_remainder_narrow_tiles(M, K, N, S, abits, dynamic, seed, codes):
     log(f"case narrow tail M={M} K={K} N={N} S={S} abits={abits} codes={codes}")
